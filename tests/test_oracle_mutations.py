@@ -1,0 +1,152 @@
+"""Each plausible mistake planted in the oracle (on the CPU, via monkeypatch)
+must make at least one pin in test_oracle_pins fail."""
+import inspect
+import math
+
+import numpy as np
+import pytest
+
+import test_oracle_pins as P
+from oracle import fdl_oracle as O
+
+
+def _pins():
+    out = []
+    for name, fn in sorted(vars(P).items()):
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if params:
+            for args in params[0].args[1]:
+                out.append((f"{name}{args}", fn, args))
+        else:
+            out.append((name, fn, ()))
+    return out
+
+
+def _failures():
+    bad = []
+    for name, fn, args in _pins():
+        try:
+            fn(*args)
+        except Exception:          # noqa: BLE001 - any failure counts
+            bad.append(name)
+    return bad
+
+
+def test_pins_all_pass_unmutated():
+    assert _failures() == []
+
+
+def _m_scale(d):
+    return 1.0 / d
+
+
+def _m_gqa(h, hq, hkv):
+    return h % hkv
+
+
+def _m_ge(c, tau):
+    return c >= tau
+
+
+def _m_order_high(cands, conf):
+    return sorted(cands, key=lambda r: (-conf[r], -r))
+
+
+_orig_visible = O.visible_keys
+
+
+def _m_drop_last_key(lp, D, mode, total):
+    return _orig_visible(lp, D, mode, total)[:-1]
+
+
+def _m_no_block(lp, D, mode, total):
+    return [k for k in _orig_visible(lp, D, mode, total) if k[1] != "block"]
+
+
+def _m_no_suffix(lp, D, mode, total):
+    return _orig_visible(lp, D, O.BLOCK_CAUSAL, total)
+
+
+def _m_prefix_off_by_one(lp, D, mode, total):
+    keys = _orig_visible(lp, D, mode, total)
+    return [(j - 1, s) if s == "cache" and j > 0 else (j, s) for j, s in keys]
+
+
+def _m_unnormalized(scores):
+    m = scores.max()
+    e = np.exp(scores - m)
+    return e, m + math.log(e.sum())
+
+
+def _m_last_argmax(row):
+    l = np.asarray(row, dtype=np.float64)
+    tok = len(l) - 1 - int(np.argmax(l[::-1]))
+    m = l[tok]
+    z = np.exp(l - m).sum()
+    top2 = np.partition(l, -2)[-2]
+    return tok, 1.0 / z, math.exp(top2 - m) / z
+
+
+def _m_conf_logit(row):
+    l = np.asarray(row, dtype=np.float64)
+    tok = int(np.argmax(l))
+    z = np.exp(l - l[tok]).sum()
+    top2 = np.partition(l, -2)[-2]
+    return tok, 1.0 / (z - 1.0 + 1e-300) if z > 1 else 1.0, math.exp(top2 - l[tok]) / z
+
+
+_orig_append = O.kv_append
+
+
+def _m_append_shift(cache, new, length):
+    cache, length2 = _orig_append(cache, new, np.asarray(length))
+    cache = np.roll(cache, 1, axis=2)
+    return cache, length2
+
+
+def _m_lm_head_transposed(x, w):
+    return O._f64(x) @ O._f64(w)
+
+
+_orig_select = O.select_rows
+
+
+def _m_factor_le(conf, masked, tau, mode=O.SELECT_THRESHOLD, k=0, factor=1.0):
+    if mode != O.SELECT_FACTOR:
+        return _orig_select(conf, masked, tau, mode, k, factor)
+    return _orig_select(conf, masked, tau, mode, k, factor + 1e-12)
+
+
+def _m_no_fallback(conf, masked, tau, mode=O.SELECT_THRESHOLD, k=0, factor=1.0):
+    if mode != O.SELECT_THRESHOLD:
+        return _orig_select(conf, masked, tau, mode, k, factor)
+    return np.asarray(masked, bool) & (np.asarray(conf) > tau)
+
+
+MUTATIONS = [
+    ("score scale 1/d instead of 1/sqrt(d)", "score_scale", _m_scale),
+    ("GQA head h % Hkv instead of h // G", "kv_head_of", _m_gqa),
+    (">= tau instead of > tau", "above_threshold", _m_ge),
+    ("ties to the higher row", "_order_by_conf", _m_order_high),
+    ("last block key dropped", "visible_keys", _m_drop_last_key),
+    ("block keys omitted", "visible_keys", _m_no_block),
+    ("DualCache suffix omitted", "visible_keys", _m_no_suffix),
+    ("prefix keys shifted by one position", "visible_keys", _m_prefix_off_by_one),
+    ("softmax not normalized", "softmax_weights", _m_unnormalized),
+    ("argmax tie to the highest id", "row_confidence", _m_last_argmax),
+    ("confidence excludes the top token from the partition", "row_confidence", _m_conf_logit),
+    ("append written one position late", "kv_append", _m_append_shift),
+    ("LM head with untransposed W", "lm_head", _m_lm_head_transposed),
+    ("factor rule <= instead of <", "select_rows", _m_factor_le),
+    ("threshold rule without fallback", "select_rows", _m_no_fallback),
+]
+
+
+@pytest.mark.parametrize("label,attr,fn", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, label, attr, fn):
+    monkeypatch.setattr(O, attr, fn)
+    bad = _failures()
+    assert bad, f"no pin caught: {label}"
