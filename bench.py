@@ -1,0 +1,214 @@
+"""Benchmark: cached block-diffusion denoising steps on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: block attention over
+the prefix cache + block, LM head, confidence select (with the commit-state
+update) and, after the last sub-block of a block, the KV append.  The default
+workload is the Qwen2.5-7B-shaped one (batch 4, 28/4 heads, d 128, prompt
+1024, answer 512, block 32, sub-block 8, vocab 152064, tau 0.9); its 64-step
+schedule is replayed until K steps have been timed.  Inputs are resident in
+HBM before timing starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise-steps/s and committed tokens/s, Qwen2.5-7B shapes; % of HBM/MFMA roof"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "lm_head_qwen2.5-7b_bs4_pmc.txt")
+LM_HEAD_SRC = os.path.join(ROOT, "block_diffusion_decoding_attn_amd", "csrc", "lm_head.hip")
+
+
+def lm_head_bytes_flops(cfg):
+    """Algorithmic bytes and flops of one LM-head launch: W, X read once, logits written once."""
+    esz = 4 if cfg.dtype == "f32" else 2
+    M = cfg.rows
+    byts = cfg.vocab * cfg.hidden * esz + M * cfg.hidden * esz + M * cfg.vocab * 4
+    flops = 2.0 * M * cfg.hidden * cfg.vocab
+    return byts, flops
+
+
+def pmc_traffic(per_launch_units=1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, scaled
+    by the copy-kernel calibration; None when missing or the kernel changed."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    kv = {}
+    for line in open(PROFILE_PMC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        sha = hashlib.sha256(open(LM_HEAD_SRC, "rb").read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_scale"])
+        return (fetch + write) * per_launch_units
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(run, budget_s: float):
+    """The oracle, as it stands, on the same workload's first steps (bounded)."""
+    import numpy as np
+    from oracle import fdl_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    cfg = run.cfg
+    kc = run.kc_host.float().numpy().copy()
+    vc = run.vc_host.float().numpy().copy()
+    length = np.full(cfg.batch, cfg.prompt_len)
+    t0 = time.perf_counter()
+    n = 0
+    commits = 0
+    for i in run.step_ids:
+        inp = run.host_inputs[i]
+        kb, vb = run.kb_host[inp.block_idx]
+        O.block_attention(inp.q, kc, vc, kb, vb, length, mode=cfg.attn_mode, total_len=cfg.cap)
+        logits = O.lm_head(inp.x, run.w_host)
+        res = O.conf_select(logits.reshape(cfg.batch, cfg.sub_block, cfg.vocab), inp.masked.numpy(),
+                            inp.tau.numpy())
+        commits += int(res["n_commit"].sum())
+        if inp.append_after:
+            kc, _ = O.kv_append(kc, kb.float().numpy(), length)
+            vc, length = O.kv_append(vc, vb.float().numpy(), length)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} steps of the {cfg.name} schedule (fp64 numpy oracle: attention, LM head, "
+                      f"select, append), {dt:.1f} s; {commits / dt:.3f} committed tokens/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1280)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="qwen2.5-7b_bs4")
+    ap.add_argument("--select", default="threshold", choices=["threshold", "topk", "factor"])
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--boost", default="calibrated", choices=["calibrated", "literal"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the batch dimension would shard across GPUs with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_diffusion_decoding_attn_amd import fdl, synth
+    from block_diffusion_decoding_attn_amd.runner import StepRunner
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fdl.lib()
+    cfg = synth.get_config(args.workload)
+    t_setup = time.perf_counter()
+    run = StepRunner(cfg, select=args.select, k=args.k, boost=args.boost, keep_host=not args.no_cpu_baseline)
+    print(f"# setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    nsched = len(run.step_ids)
+
+    # commits per schedule step (deterministic: the same inputs every pass)
+    run.reset()
+    commits = []
+    for i in run.step_ids:
+        run.step(i)
+        commits.append(int(run.n_commit.sum()))
+    torch.cuda.synchronize()
+
+    def do_steps(n, start, ev=None):
+        pos = start
+        for j in range(n):
+            if pos == 0:
+                run.reset()
+            i = run.step_ids[pos]
+            inp = run.inputs[i]
+            if run.dual and inp.sub_idx == 0:
+                run.refresh_block(inp.block_idx)
+            run.attention(i)
+            if ev is not None:
+                ev[j][0].record()
+            run.lm_head(i)
+            if ev is not None:
+                ev[j][1].record()
+            run.select(i)
+            if inp.append_after and not run.dual:
+                run.append(i)
+            pos = (pos + 1) % nsched
+        return pos
+
+    pos = do_steps(args.warmup, 0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start_pos = pos
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    do_steps(args.steps, start_pos, ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end)
+    ms_per_step = ms / args.steps
+    committed = sum(commits[(start_pos + j) % nsched] for j in range(args.steps))
+    lm_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    byts, flops = lm_head_bytes_flops(cfg)
+    ai = flops / byts
+    if ai > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": flops / (lm_ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byts / (lm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = pmc_traffic()
+    roof["kernel"] = "fdl_lm_head"
+    roof["kernel_us"] = lm_ms * 1e3
+    roof["algorithmic_bytes"] = byts
+
+    out = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "prompt_len": cfg.prompt_len, "gen_len": cfg.gen_len,
+                   "block": cfg.block, "sub_block": cfg.sub_block, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "hidden": cfg.hidden, "vocab": cfg.vocab,
+                   "attn_mode": cfg.attn_mode, "select": args.select, "tau": list(cfg.tau), "boost": args.boost,
+                   "parallelism": "single-gpu"},
+        "committed_tokens_per_s": committed / (ms * 1e-3),
+        "commits_per_step": committed / args.steps,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(run, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+// C ABI entry points of libfdl: host-side validation, then kernel launches.
+// Nothing here allocates device memory or synchronizes with the device.
+#include "common.h"
+
+namespace fdl {
+
+size_t attn_workspace_bytes(const fdl_dims& d);
+int attn_max_rows();
+int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc, const void* vc,
+                const int32_t* prefix_len, const void* kb, const void* vb, void* out, float* lse, void* ws,
+                size_t ws_bytes, hipStream_t st);
+int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, hipStream_t st);
+size_t select_workspace_bytes(const fdl_dims& d, int rows_per_seq);
+int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* masked, const float* tau, int mode,
+                  int k, float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out, int32_t* n_commit,
+                  int32_t* tokens_inout, uint8_t* masked_inout, void* ws, size_t ws_bytes, hipStream_t st);
+int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int n_new, int32_t* len,
+                  hipStream_t st);
+
+int dtype_size(int dtype) { return dtype == FDL_F32 ? 4 : 2; }
+
+int check_launch() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FDL_OK : FDL_E_HIP;
+}
+
+// Checks shared by every entry point.
+static int check_dims(const fdl_dims* d) {
+  if (!d) return FDL_E_INVAL;
+  if (d->batch < 1 || d->prompt_len < 0 || d->gen_len < 1 || d->block < 1 || d->sub_block < 1) return FDL_E_INVAL;
+  if (d->block % d->sub_block != 0 || d->gen_len % d->block != 0) return FDL_E_INVAL;
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0) return FDL_E_INVAL;
+  if (d->head_dim < 1 || d->hidden < 1 || d->vocab < 1) return FDL_E_INVAL;
+  if (d->dtype != FDL_F32 && d->dtype != FDL_BF16) return FDL_E_INVAL;
+  if (d->attn_mode != FDL_ATTN_BLOCK_CAUSAL && d->attn_mode != FDL_ATTN_DUAL_CACHE) return FDL_E_INVAL;
+  // size limits that keep every index inside 32-bit arithmetic where it is used
+  const long long cap = (long long)d->prompt_len + d->gen_len;
+  if (cap > (1 << 24) || d->vocab > (1 << 28) || d->hidden > (1 << 20)) return FDL_E_UNSUPPORTED;
+  if (d->batch > 65535 || d->n_kv_heads > 32767) return FDL_E_UNSUPPORTED;  // grid y/z extents
+  if (d->head_dim != 64 && d->head_dim != 128) return FDL_E_UNSUPPORTED;
+  return FDL_OK;
+}
+
+}  // namespace fdl
+
+using namespace fdl;
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int fdl_version(void) { return 100; }
+
+const char* fdl_strerror(int status) {
+  switch (status) {
+    case FDL_OK: return "ok";
+    case FDL_E_INVAL: return "invalid argument";
+    case FDL_E_UNSUPPORTED: return "unsupported argument combination";
+    case FDL_E_HIP: return "HIP launch error";
+    case FDL_E_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int fdl_dims_check(const fdl_dims* dims) { return check_dims(dims); }
+
+size_t fdl_block_attn_workspace_size(const fdl_dims* dims) {
+  if (check_dims(dims) != FDL_OK) return 0;
+  return attn_workspace_bytes(*dims);
+}
+
+int fdl_block_attn(const fdl_dims* dims, int32_t block_idx, int32_t sub_idx, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* prefix_len, const void* k_blk, const void* v_blk, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  if (block_idx < 0 || block_idx >= d.gen_len / d.block) return FDL_E_INVAL;
+  if (sub_idx < 0 || sub_idx >= d.block / d.sub_block) return FDL_E_INVAL;
+  if (!q || !k_cache || !v_cache || !k_blk || !v_blk || !out) return FDL_E_INVAL;
+  if ((d.n_q_heads / d.n_kv_heads) * d.sub_block > attn_max_rows()) return FDL_E_UNSUPPORTED;
+  return attn_launch(d, block_idx, q, k_cache, v_cache, prefix_len, k_blk, v_blk, out, lse, workspace,
+                     workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int fdl_lm_head(const fdl_dims* dims, int32_t rows, const void* x, const void* w, float* logits, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  if (rows < 1 || !x || !w || !logits) return FDL_E_INVAL;
+  if (d.dtype == FDL_BF16 && d.hidden % 64 != 0) return FDL_E_UNSUPPORTED;
+  if (d.dtype == FDL_F32 && (d.hidden % 4 != 0 || rows > 64)) return FDL_E_UNSUPPORTED;
+  if ((long long)rows * d.vocab > (1LL << 40)) return FDL_E_UNSUPPORTED;
+  return lm_head_launch(d, rows, x, w, logits, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t fdl_conf_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq) {
+  if (check_dims(dims) != FDL_OK || rows_per_seq < 1 || rows_per_seq > 256) return 0;
+  return select_workspace_bytes(*dims, rows_per_seq);
+}
+
+int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* logits, const uint8_t* masked,
+                    const float* tau, int32_t mode, int32_t k, float factor, int32_t* token_out, float* conf_out,
+                    uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  if (rows_per_seq < 1 || rows_per_seq > 256) return FDL_E_INVAL;
+  if (!logits || !masked || !token_out || !conf_out || !commit_out || !n_commit) return FDL_E_INVAL;
+  if (mode == FDL_SELECT_THRESHOLD) {
+    if (!tau) return FDL_E_INVAL;
+  } else if (mode == FDL_SELECT_TOPK) {
+    if (k < 1) return FDL_E_INVAL;
+  } else if (mode == FDL_SELECT_FACTOR) {
+    if (!(factor > 0.f)) return FDL_E_INVAL;
+  } else {
+    return FDL_E_INVAL;
+  }
+  if ((long long)d.batch * rows_per_seq > 65535) return FDL_E_UNSUPPORTED;  // grid y extent
+  return select_launch(d, rows_per_seq, logits, masked, tau, mode, k, factor, token_out, conf_out, commit_out,
+                       n_commit, tokens_inout, masked_inout, workspace, workspace_bytes,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  int32_t n_new, int32_t* len, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  if (!k_cache || !v_cache || !k_new || !v_new || !len) return FDL_E_INVAL;
+  if (n_new < 1 || n_new > d.prompt_len + d.gen_len) return FDL_E_INVAL;
+  return append_launch(d, k_cache, v_cache, k_new, v_new, n_new, len, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,63 @@
+// KV append: write a finished block's K/V into the block-level cache.
+//
+// "Fast-dLLM v2: Efficient Block-Diffusion LLM", Inference Pipeline Level 3:
+// once a block is fully decoded its K/V are stored and reused unchanged by all
+// later blocks.  "Fast-dLLM: Reusing Bidirectional State ...", Algorithm 1:
+// the per-block refresh rewrites the cached regions (len = 0, then append all
+// P + L positions).
+//
+// A bitwise copy: 16-byte vector loads and stores over (sequence, K|V x head,
+// chunk) work items; a second one-thread-per-sequence kernel advances len[b]
+// after every copy of the step has been issued on the stream, so no copy can
+// see a half-updated length.
+#include "common.h"
+
+namespace fdl {
+
+struct AppendArgs {
+  void* kc;
+  void* vc;
+  const void* kn;
+  const void* vn;
+  int32_t* len;
+  int B, Hkv, cap, n_new;
+  int row_bytes;  // head_dim * element size
+};
+
+__global__ __launch_bounds__(256) void kv_append_copy_kernel(AppendArgs a) {
+  const int b = blockIdx.z;
+  const int kv = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
+  const int lo = a.len[b];
+  if (lo < 0 || lo > a.cap - a.n_new) return;  // would overflow: leave the sequence untouched
+  const size_t pair = size_t(b) * a.Hkv + g;
+  const char* src = reinterpret_cast<const char*>(kv ? a.vn : a.kn) + pair * a.n_new * size_t(a.row_bytes);
+  char* dst = reinterpret_cast<char*>(kv ? a.vc : a.kc) + (pair * a.cap + lo) * size_t(a.row_bytes);
+  const size_t n16 = size_t(a.n_new) * a.row_bytes / 16;
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
+    st16(dst + i * 16, ld16(src + i * 16));
+}
+
+__global__ void kv_append_len_kernel(int32_t* len, int B, int cap, int n_new) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int lo = len[b];
+  if (lo < 0 || lo > cap - n_new) return;
+  len[b] = lo + n_new;
+}
+
+int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int n_new, int32_t* len,
+                  hipStream_t st) {
+  AppendArgs a;
+  a.kc = kc; a.vc = vc; a.kn = kn; a.vn = vn; a.len = len;
+  a.B = d.batch; a.Hkv = d.n_kv_heads; a.cap = d.prompt_len + d.gen_len; a.n_new = n_new;
+  a.row_bytes = d.head_dim * dtype_size(d.dtype);
+  const size_t n16 = size_t(n_new) * a.row_bytes / 16;
+  int chunks = int((n16 + 255) / 256);
+  if (chunks > 64) chunks = 64;
+  hipLaunchKernelGGL(kv_append_copy_kernel, dim3(chunks, 2 * d.n_kv_heads, d.batch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(kv_append_len_kernel, dim3((d.batch + 255) / 256), dim3(256), 0, st, len, d.batch, a.cap,
+                     n_new);
+  return check_launch();
+}
+
+}  // namespace fdl

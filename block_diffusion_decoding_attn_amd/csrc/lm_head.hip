@@ -1,0 +1,310 @@
+// LM head: logits[M][V] = X[M][H] . W[V][H]^T with fp32 accumulation.
+//
+// "Fast-dLLM v2: Efficient Block-Diffusion LLM", Inference Pipeline Level 2:
+// every position of the active block gets a probability distribution over the
+// vocabulary; this kernel produces its logits.
+//
+// Two regimes on gfx950 (ridge ~312 flop/B for bf16 MFMA at 8 TB/s):
+//   * skinny (M <= 64, the per-step rows of one or a few sequences): 2M flop
+//     per weight element, far below the ridge, so the kernel is a weight
+//     stream.  Each wave owns a run of vocabulary rows and streams them once
+//     with 16-byte non-temporal loads, several k-steps in flight, feeding
+//     MFMA (A = W rows, B = X^T).  X (<= 64 x H) stays in L2.
+//   * tiled (M > 64): MFMA-bound; 128 x 128 output tiles per workgroup, K
+//     staged through LDS in 64-wide slabs, 32x32x16 bf16 MFMA.
+#include "common.h"
+
+namespace fdl {
+
+struct LmArgs {
+  const void* x;
+  const void* w;
+  float* out;
+  int M, H, V;
+};
+
+// ---------------------------------------------------------------------------
+// skinny: NTM M-tiles of 16 columns, RT vocab tiles of 16 rows per wave,
+// PF k-steps of loads in flight.
+template <int NTM, int RT, int PF, int WPB>
+__global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wave_id = blockIdx.x * WPB + (threadIdx.x >> 6);
+  const int v0 = wave_id * RT * 16;
+  if (v0 >= a.V) return;
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
+
+  const bf16_t* wp[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    int row = v0 + t * 16 + l16;
+    row = row < a.V ? row : a.V - 1;
+    wp[t] = W + size_t(row) * a.H + 8 * grp;
+  }
+  const bf16_t* xp[NTM];
+  bool xok[NTM];
+#pragma unroll
+  for (int n = 0; n < NTM; ++n) {
+    const int m = n * 16 + l16;
+    xok[n] = m < a.M;
+    xp[n] = X + size_t(xok[n] ? m : 0) * a.H + 8 * grp;
+  }
+
+  f32x4 acc[RT][NTM];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int n = 0; n < NTM; ++n) acc[t][n] = f32x4{0, 0, 0, 0};
+
+  const int nk = a.H / 32;
+  u32x4 wa[PF][RT], xb[PF][NTM];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    if (s < nk) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) wa[s][t] = ld16_stream(wp[t] + s * 32);
+#pragma unroll
+      for (int n = 0; n < NTM; ++n) xb[s][n] = xok[n] ? ld16(xp[n] + s * 32) : u32x4{0, 0, 0, 0};
+    }
+  }
+  for (int k0 = 0; k0 < nk; k0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int ks = k0 + s;
+      if (ks < nk) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int n = 0; n < NTM; ++n) acc[t][n] = mfma16x16x32_bf16(wa[s][t], xb[s][n], acc[t][n]);
+        const int kn = ks + PF;
+        if (kn < nk) {
+#pragma unroll
+          for (int t = 0; t < RT; ++t) wa[s][t] = ld16_stream(wp[t] + kn * 32);
+#pragma unroll
+          for (int n = 0; n < NTM; ++n) xb[s][n] = xok[n] ? ld16(xp[n] + kn * 32) : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+
+  // lane holds C[vocab v0 + 16t + 4grp + e][m = 16n + l16]
+#pragma unroll
+  for (int n = 0; n < NTM; ++n) {
+    const int m = n * 16 + l16;
+    if (m >= a.M) continue;
+    float* orow = a.out + size_t(m) * a.V;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int v = v0 + t * 16 + grp * 4;
+      if (v + 3 < a.V && (a.V & 3) == 0) {
+        *reinterpret_cast<f32x4*>(orow + v) = acc[t][n];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v + e < a.V) orow[v + e] = acc[t][n][e];
+      }
+    }
+  }
+}
+
+// f32 data (the small fp32 workload): same wave decomposition on the
+// 16x16x4 f32 MFMA, one k value per lane per instruction.
+template <int NTM, int RT>
+__global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int v0 = wave_id * RT * 16;
+  if (v0 >= a.V) return;
+  const float* W = reinterpret_cast<const float*>(a.w);
+  const float* X = reinterpret_cast<const float*>(a.x);
+  f32x4 acc[RT][NTM];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int n = 0; n < NTM; ++n) acc[t][n] = f32x4{0, 0, 0, 0};
+  for (int k = 0; k < a.H; k += 4) {
+    float xa[NTM];
+#pragma unroll
+    for (int n = 0; n < NTM; ++n) {
+      const int m = n * 16 + l16;
+      xa[n] = m < a.M ? X[size_t(m) * a.H + k + grp] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      int row = v0 + t * 16 + l16;
+      row = row < a.V ? row : a.V - 1;
+      const float wv = W[size_t(row) * a.H + k + grp];
+#pragma unroll
+      for (int n = 0; n < NTM; ++n) acc[t][n] = mfma16x16x4_f32(wv, xa[n], acc[t][n]);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NTM; ++n) {
+    const int m = n * 16 + l16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = v0 + t * 16 + grp * 4 + e;
+        if (v < a.V) a.out[size_t(m) * a.V + v] = acc[t][n][e];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tiled: workgroup tile 128 (vocab) x 128 (rows), 4 waves of 64 x 64, K slabs
+// of 64 through LDS with the next slab prefetched into registers.
+constexpr int TB_V = 128, TB_M = 128, TB_K = 64, TB_PAD = 8, TB_ST = TB_K + TB_PAD;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void lm_head_tiled_bf16(LmArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[TB_V * TB_ST];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[TB_M * TB_ST];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+  // give each XCD a contiguous run of tiles, row tiles fastest, so that the
+  // row tiles sharing a weight tile meet in the same L2.
+  const int nvt = (a.V + TB_V - 1) / TB_V, nmt = (a.M + TB_M - 1) / TB_M;
+  const int ntiles = nvt * nmt, per_xcd = (ntiles + 7) / 8;
+  const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tile >= ntiles) return;
+  const int vt = tile / nmt, mt = tile % nmt;
+  const int v0 = vt * TB_V, m0 = mt * TB_M;
+  const int wv = (wave & 1) * 64, wm = (wave >> 1) * 64;
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
+
+  // each thread stages 4 chunks of A and 4 of B per slab (128 rows x 8 chunks)
+  const bf16_t* ap[4];
+  const bf16_t* bp[4];
+  bool bok[4];
+  int srow[4], scol[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ch = tid + c * 256;
+    srow[c] = ch >> 3;
+    scol[c] = (ch & 7) * 8;
+    int vr = v0 + srow[c];
+    vr = vr < a.V ? vr : a.V - 1;
+    ap[c] = W + size_t(vr) * a.H + scol[c];
+    const int mr = m0 + srow[c];
+    bok[c] = mr < a.M;
+    bp[c] = X + size_t(bok[c] ? mr : 0) * a.H + scol[c];
+  }
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int k) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ra[c] = ld16(ap[c] + k);
+      rb[c] = bok[c] ? ld16(bp[c] + k) : u32x4{0, 0, 0, 0};
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  gload(0);
+  for (int k = 0; k < a.H; k += TB_K) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      *reinterpret_cast<u32x4*>(&As[srow[c] * TB_ST + scol[c]]) = ra[c];
+      *reinterpret_cast<u32x4*>(&Bs[srow[c] * TB_ST + scol[c]]) = rb[c];
+    }
+    __syncthreads();
+    if (k + TB_K < a.H) gload(k + TB_K);
+#pragma unroll
+    for (int kk = 0; kk < TB_K; kk += 16) {
+      u32x4 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(&As[(wv + i * 32 + l32) * TB_ST + kk + 8 * half]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(&Bs[(wm + j * 32 + l32) * TB_ST + kk + 8 * half]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                              __builtin_bit_cast(bf16x8, bf[j]), acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + wm + j * 32 + l32;
+    if (m >= a.M) continue;
+    float* orow = a.out + size_t(m) * a.V;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = v0 + wv + i * 32 + q * 8 + half * 4;
+        const f32x4 val{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (v + 3 < a.V && (a.V & 3) == 0) {
+          *reinterpret_cast<f32x4*>(orow + v) = val;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v + e < a.V) orow[v + e] = val[e];
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+template <int NTM>
+static void launch_skinny_bf16(const LmArgs& a, hipStream_t st) {
+  constexpr int RT = 4, PF = 4, WPB = 4;
+  const int waves = (a.V + RT * 16 - 1) / (RT * 16);
+  hipLaunchKernelGGL((lm_head_skinny_bf16<NTM, RT, PF, WPB>), dim3((waves + WPB - 1) / WPB), dim3(WPB * 64), 0, st,
+                     a);
+}
+
+template <int NTM>
+static void launch_skinny_f32(const LmArgs& a, hipStream_t st) {
+  constexpr int RT = 2;
+  const int waves = (a.V + RT * 16 - 1) / (RT * 16);
+  hipLaunchKernelGGL((lm_head_skinny_f32<NTM, RT>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
+}
+
+int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, hipStream_t st) {
+  LmArgs a{x, w, logits, rows, d.hidden, d.vocab};
+  const int ntm = (rows + 15) / 16;
+  if (d.dtype == FDL_BF16) {
+    switch (ntm) {
+      case 1: launch_skinny_bf16<1>(a, st); break;
+      case 2: launch_skinny_bf16<2>(a, st); break;
+      case 3: launch_skinny_bf16<3>(a, st); break;
+      case 4: launch_skinny_bf16<4>(a, st); break;
+      default: {
+        const int nvt = (a.V + TB_V - 1) / TB_V, nmt = (rows + TB_M - 1) / TB_M;
+        hipLaunchKernelGGL(lm_head_tiled_bf16, dim3(8 * ((nvt * nmt + 7) / 8)), dim3(256), 0, st, a);
+      }
+    }
+  } else {
+    if (ntm > 4) return FDL_E_UNSUPPORTED;
+    switch (ntm) {
+      case 1: launch_skinny_f32<1>(a, st); break;
+      case 2: launch_skinny_f32<2>(a, st); break;
+      case 3: launch_skinny_f32<3>(a, st); break;
+      default: launch_skinny_f32<4>(a, st); break;
+    }
+  }
+  return check_launch();
+}
+
+}  // namespace fdl

@@ -1,0 +1,145 @@
+"""Device buffers and call sequence of a workload's denoising steps.
+
+A step is the whole hot path over one batch: fdl_block_attn, fdl_lm_head,
+fdl_conf_select and, after the last step of a block, fdl_kv_append.  For the
+v1 DualCache workload every block starts with the refresh, which rewrites the
+whole cache through fdl_kv_append (len = 0, then P + L positions).
+
+The hidden rows fed to the LM head are synthetic (the transformer layers
+between attention and the LM head are not part of the step), so the attention
+output and the LM-head input are independent buffers.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import torch
+
+from . import fdl, synth
+
+
+@dataclasses.dataclass
+class StepInputs:
+    q: torch.Tensor          # [B][S][Hq][d]
+    x: torch.Tensor          # [B*S][H]
+    masked: torch.Tensor     # [B][S] uint8
+    tau: torch.Tensor        # [B] f32
+    block_idx: int
+    sub_idx: int
+    append_after: bool
+
+
+class StepRunner:
+    """Holds one workload's device state and enqueues its steps.
+
+    select: "threshold" (Algorithm 2), "topk" (fixed count `k`) or "factor".
+    """
+
+    def __init__(self, cfg: synth.Config, seed: int = 0, boost: str = "calibrated", select: str = "threshold",
+                 k: int = 4, factor: float = 1.0, device: str = "cuda", steps: Optional[List[int]] = None,
+                 keep_host: bool = False):
+        self.cfg, self.seed, self.boost = cfg, seed, boost
+        self.select_mode = {"threshold": fdl.FDL_SELECT_THRESHOLD, "topk": fdl.FDL_SELECT_TOPK,
+                            "factor": fdl.FDL_SELECT_FACTOR}[select]
+        self.k, self.factor = k, factor
+        self.dims = fdl.make_dims(cfg)
+        self.dev = torch.device(device)
+        self.sched = synth.schedule(cfg)
+        self.dual = cfg.attn_mode == synth.DUAL_CACHE
+        B, S, cap = cfg.batch, cfg.sub_block, cfg.cap
+        dt = cfg.torch_dtype
+
+        self.w_host = synth.weights(cfg, seed)
+        self.w = self.w_host.to(self.dev)
+        fill = cfg.prompt_len
+        kc, vc = synth.kv_cache(cfg, seed, fill=None if self.dual else fill)
+        self.kc_host, self.vc_host = (kc, vc) if keep_host else (None, None)
+        self.k_cache, self.v_cache = kc.to(self.dev), vc.to(self.dev)
+        self.len = torch.full((B,), fill, dtype=torch.int32, device=self.dev)
+
+        self.step_ids = list(range(len(self.sched))) if steps is None else list(steps)
+        self.blocks = sorted({self.sched[i][0] for i in self.step_ids})
+        self.kb_host: Dict[int, tuple] = {}
+        self.k_blk: Dict[int, torch.Tensor] = {}
+        self.v_blk: Dict[int, torch.Tensor] = {}
+        self.refresh: Dict[int, tuple] = {}
+        for b in self.blocks:
+            kb, vb = synth.block_kv(cfg, b, seed)
+            if keep_host:
+                self.kb_host[b] = (kb, vb)
+            self.k_blk[b], self.v_blk[b] = kb.to(self.dev), vb.to(self.dev)
+            if self.dual:
+                kr, vr = synth.refresh_kv(cfg, b, seed)
+                self.refresh[b] = (kr.to(self.dev), vr.to(self.dev), (kr, vr) if keep_host else None)
+        self.inputs: Dict[int, StepInputs] = {}
+        self.host_inputs: Dict[int, StepInputs] = {}
+        # masked state of every step: the select updates it in place (committed
+        # rows leave the masked set); reset() restores the initial state
+        masks = [synth.masked_rows(cfg, i, seed) for i in self.step_ids]
+        self.masked_init = torch.stack(masks).to(self.dev)
+        self.masked_all = self.masked_init.clone()
+        for n, i in enumerate(self.step_ids):
+            b, s, app = self.sched[i]
+            q = synth.queries(cfg, i, seed)
+            x, _, _ = synth.hidden_rows(cfg, self.w_host, i, seed, boost)
+            t = synth.taus(cfg, i, seed)
+            if keep_host:
+                self.host_inputs[i] = StepInputs(q, x, masks[n], t, b, s, app)
+            self.inputs[i] = StepInputs(q.to(self.dev), x.to(self.dev), self.masked_all[n], t.to(self.dev), b, s,
+                                        app)
+
+        # outputs / workspaces
+        self.out = torch.empty((B, S, cfg.n_q_heads, cfg.head_dim), dtype=dt, device=self.dev)
+        self.lse = torch.empty((B, cfg.n_q_heads, S), dtype=torch.float32, device=self.dev)
+        self.logits = torch.empty((B * S, cfg.vocab), dtype=torch.float32, device=self.dev)
+        self.token = torch.empty((B, S), dtype=torch.int32, device=self.dev)
+        self.conf = torch.empty((B, S), dtype=torch.float32, device=self.dev)
+        self.commit = torch.empty((B, S), dtype=torch.uint8, device=self.dev)
+        self.n_commit = torch.empty((B,), dtype=torch.int32, device=self.dev)
+        self.tokens = torch.zeros((B, S), dtype=torch.int32, device=self.dev)
+        ws_a = fdl.fdl_block_attn_workspace_size(self.dims)
+        ws_s = fdl.fdl_conf_select_workspace_size(self.dims, S)
+        self.ws_attn = torch.empty((max(ws_a, 16),), dtype=torch.uint8, device=self.dev)
+        self.ws_sel = torch.empty((max(ws_s, 16),), dtype=torch.uint8, device=self.dev)
+
+    # -- the step ------------------------------------------------------------
+    def reset(self):
+        """Back to the start of the schedule: the cache holds only the prompt and
+        every step's rows are masked as initially drawn."""
+        self.len.fill_(self.cfg.prompt_len)
+        self.masked_all.copy_(self.masked_init)
+
+    def refresh_block(self, b: int):
+        """v1 DualCache refresh before block b: len = 0, rewrite all P + L positions."""
+        kr, vr, _ = self.refresh[b]
+        self.len.zero_()
+        fdl.fdl_kv_append(self.dims, self.k_cache, self.v_cache, kr, vr, self.len)
+
+    def attention(self, i: int):
+        inp = self.inputs[i]
+        fdl.fdl_block_attn(self.dims, inp.block_idx, inp.sub_idx, inp.q, self.k_cache, self.v_cache, None,
+                           self.k_blk[inp.block_idx], self.v_blk[inp.block_idx], self.out, self.lse, self.ws_attn)
+
+    def lm_head(self, i: int):
+        fdl.fdl_lm_head(self.dims, self.inputs[i].x, self.w, self.logits)
+
+    def select(self, i: int):
+        inp = self.inputs[i]
+        fdl.fdl_conf_select(self.dims, self.cfg.sub_block, self.logits, inp.masked, inp.tau, self.select_mode,
+                            self.k, self.factor, self.token, self.conf, self.commit, self.n_commit, self.tokens,
+                            inp.masked, self.ws_sel)
+
+    def append(self, i: int):
+        b = self.inputs[i].block_idx
+        fdl.fdl_kv_append(self.dims, self.k_cache, self.v_cache, self.k_blk[b], self.v_blk[b], self.len)
+
+    def step(self, i: int):
+        inp = self.inputs[i]
+        if self.dual and inp.sub_idx == 0:
+            self.refresh_block(inp.block_idx)
+        self.attention(i)
+        self.lm_head(i)
+        self.select(i)
+        if inp.append_after and not self.dual:
+            self.append(i)

@@ -1,0 +1,196 @@
+/*
+ * fdl.h -- C ABI of libfdl, the MI355X (gfx950) cached block-diffusion
+ * denoising step of Fast-dLLM / Fast-dLLM v2.
+ *
+ * One denoising step is four calls, enqueued in order on one HIP stream:
+ *   fdl_block_attn   attention of the active (sub-)block's query rows over the
+ *                    block-level prefix KV cache and the block itself (and, in
+ *                    the v1 DualCache mode, the cached suffix)
+ *   fdl_lm_head      hidden rows -> vocabulary logits
+ *   fdl_conf_select  greedy token, confidence, commit set per sequence
+ *   fdl_kv_append    append a finished block's K/V to the cache
+ *
+ * Pages defining the operations (cited by title and section):
+ *   "Fast-dLLM v2: Efficient Block-Diffusion LLM" (technical breakdown):
+ *     Attention Mask Design, Inference-time attention mask (Figure 7b),
+ *     Inference Pipeline Levels 1-3, Batch decoding with length padding,
+ *     Sub-block size as a decoding granularity knob.
+ *   "Fast-dLLM: Reusing Bidirectional State and Spending Confidence on
+ *     Parallel Tokens": eq 3, section 3 (PrefixCache and DualCache,
+ *     Algorithm 1), section 4 (Algorithm 2), section 6 (eq 13, Algorithm 3).
+ *   "Diffusion language models: review questions": commit rule, fixed count.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers owned by the caller (except `dims`, which
+ *     is a host pointer read during the call).  The library allocates no
+ *     memory and keeps no global mutable state; calls are reentrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     No call synchronizes with the host or reads device memory back.
+ *   - Validation of scalar arguments and pointers happens on the host before
+ *     anything is launched; on failure the call returns a negative fdl_status
+ *     and launches nothing.  Values held in device memory (lengths, tau) are
+ *     the caller's contract; the kernels never access memory outside the
+ *     extents stated below, whatever those values are.
+ *   - After launching, a HIP launch error is reported as FDL_E_HIP.
+ *   - Tensors are dense, row-major, in the layouts given per argument.
+ *     bf16 = bfloat16 stored as 16-bit words; f32 = IEEE binary32.
+ */
+#ifndef FDL_H
+#define FDL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FDL_OK = 0,
+  FDL_E_INVAL = -1,        /* a scalar or pointer argument is invalid           */
+  FDL_E_UNSUPPORTED = -2,  /* valid but not supported (e.g. head_dim 96)        */
+  FDL_E_HIP = -3,          /* a HIP launch reported an error                    */
+  FDL_E_WORKSPACE = -4     /* workspace missing or smaller than required        */
+} fdl_status;
+
+typedef enum { FDL_F32 = 0, FDL_BF16 = 1 } fdl_dtype;
+
+typedef enum {
+  /* Fast-dLLM v2, Figure 7b: the active block attends bidirectionally to its
+     own D positions and to the whole cached prefix; nothing after it. */
+  FDL_ATTN_BLOCK_CAUSAL = 0,
+  /* Fast-dLLM v1 DualCache (section 3): prefix cache + fresh block + cached
+     suffix of all later positions up to P + L; fully bidirectional. */
+  FDL_ATTN_DUAL_CACHE = 1
+} fdl_attn_mode;
+
+typedef enum {
+  /* Algorithm 2: commit every candidate with conf > tau (strict); if none,
+     the single most confident candidate (lowest row on equal conf). */
+  FDL_SELECT_THRESHOLD = 0,
+  /* fixed count: the min(k, #candidates) most confident candidates (lowest
+     row first on equal conf). */
+  FDL_SELECT_TOPK = 1,
+  /* eq 13 / Algorithm 3: candidates sorted by decreasing conf; commit the
+     first n for the largest n with (n+1)(1 - c_(n)) < factor, else the first. */
+  FDL_SELECT_FACTOR = 2
+} fdl_select_mode;
+
+/* The problem statement of one decoding run.
+ *   batch       B, sequences decoded together (right-padded to whole blocks)
+ *   prompt_len  P, cached prompt positions
+ *   gen_len     L, answer positions (a multiple of block)
+ *   block       D, block size (32 on the pages)
+ *   sub_block   S, query rows per step (8 on the pages; = block for whole-block steps);
+ *               block % sub_block == 0
+ *   n_q_heads   Hq; n_kv_heads Hkv divides Hq (query head h reads KV head h / (Hq/Hkv))
+ *   head_dim    d, 64 or 128
+ *   hidden      H, LM-head input width (a multiple of 32 for bf16, of 4 for f32)
+ *   vocab       V
+ *   dtype       fdl_dtype of Q/K/V/O, X and W
+ *   attn_mode   fdl_attn_mode
+ * The KV cache of one sequence and KV head holds cap = P + L positions. */
+typedef struct fdl_dims {
+  int32_t batch;
+  int32_t prompt_len;
+  int32_t gen_len;
+  int32_t block;
+  int32_t sub_block;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t hidden;
+  int32_t vocab;
+  int32_t dtype;
+  int32_t attn_mode;
+} fdl_dims;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int fdl_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* fdl_strerror(int status);
+
+/* Host-side validation of `dims` alone.  Returns FDL_OK or the code the entry
+ * points would return for these dims. */
+int fdl_dims_check(const fdl_dims* dims);
+
+/* Bytes of device workspace fdl_block_attn needs for any block_idx/sub_idx
+ * of `dims` (0 if none).  Returns 0 for invalid dims. */
+size_t fdl_block_attn_workspace_size(const fdl_dims* dims);
+
+/* Block attention: eq 3 (softmax(Q K^T / sqrt(d)) V) over the visible keys of
+ * the active block (Figure 7b mask, or DualCache), GQA, exact online softmax.
+ *
+ *   block_idx   index b of the active block, 0 <= b < L / D
+ *   sub_idx     index of the active sub-block, 0 <= sub_idx < D / S
+ *               (every row of a block sees the same keys, so it only checks range)
+ *   q           [B][S][Hq][d]  query rows of the active sub-block (dtype)
+ *   k_cache     [B][Hkv][P+L][d] (dtype); v_cache likewise.  Position j holds
+ *               the K/V of absolute position j.  Read: prefix positions
+ *               [0, Lp) and, in DualCache mode, the suffix [Lp + D, P + L).
+ *   prefix_len  [B] int32 Lp per sequence, or NULL for Lp = P + b*D for all.
+ *               Contract: 0 <= Lp and Lp + D <= P + L (values outside are clamped).
+ *   k_blk       [B][Hkv][D][d] fresh K of the active block's D positions; v_blk likewise
+ *   out         [B][S][Hq][d] (dtype), written
+ *   lse         [B][Hq][S] f32 natural-log log-sum-exp of the scores, or NULL
+ *   workspace   >= fdl_block_attn_workspace_size(dims) bytes (may be NULL if that is 0)
+ * The query rows may be any subset of the block: each sees Lp + D keys
+ * (block-causal) or P + L keys (DualCache). */
+int fdl_block_attn(const fdl_dims* dims, int32_t block_idx, int32_t sub_idx,
+                   const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* prefix_len, const void* k_blk, const void* v_blk,
+                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* LM head: logits[r][v] = sum_k X[r][k] * W[v][k], f32 accumulation and
+ * output ("Fast-dLLM v2", Inference Pipeline Level 2: a distribution over the
+ * vocabulary per position; with the token shift of Step 5 the row for block
+ * position i is the hidden state at i - 1, which is the caller's row choice).
+ *   rows    M >= 1
+ *   x       [M][H] (dtype)
+ *   w       [V][H] (dtype)
+ *   logits  [M][V] f32, written */
+int fdl_lm_head(const fdl_dims* dims, int32_t rows, const void* x, const void* w,
+                float* logits, void* stream);
+
+/* Bytes of device workspace fdl_conf_select needs (0 for invalid arguments). */
+size_t fdl_conf_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq);
+
+/* Confidence select (Algorithm 2 / fixed count / Algorithm 3) with the
+ * commit-state update.
+ *   rows_per_seq R, 1 <= R <= 256; row r of sequence b is logits row b*R + r
+ *   logits       [B][R][V] f32 (finite values)
+ *   masked       [B][R] uint8, nonzero = still [MASK] = a commit candidate
+ *   tau          [B] f32 threshold per sequence (FDL_SELECT_THRESHOLD)
+ *   mode         fdl_select_mode; k for TOPK (>= 1); factor for FACTOR (> 0)
+ *   token_out    [B][R] int32 argmax token of every row (lowest id on ties)
+ *   conf_out     [B][R] f32 its softmax probability, 1 / sum_v exp(l_v - l_max)
+ *   commit_out   [B][R] uint8 1 = committed this step (only candidates)
+ *   n_commit     [B] int32 number committed (>= 1 whenever a row is masked)
+ *   tokens_inout [B][R] int32 or NULL: committed rows take their token
+ *   masked_inout [B][R] uint8 or NULL: committed rows are cleared; may alias masked
+ *   workspace    >= fdl_conf_select_workspace_size(dims, R) bytes */
+int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* logits,
+                    const uint8_t* masked, const float* tau, int32_t mode, int32_t k,
+                    float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out,
+                    int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* KV append ("Fast-dLLM v2", Level 3 block-level cache: a finished block's
+ * K/V are stored for all later steps; Fast-dLLM Algorithm 1: the refresh
+ * rewrites the cached regions, i.e. len = 0 then append P + L positions).
+ *   k_cache, v_cache [B][Hkv][P+L][d] (dtype), written at [len[b], len[b] + n_new)
+ *   k_new, v_new     [B][Hkv][n_new][d] (dtype)
+ *   n_new            1 <= n_new <= P + L
+ *   len              [B] int32, read then advanced by n_new.  A sequence with
+ *                    len[b] < 0 or len[b] + n_new > P + L is left untouched
+ *                    (no write, len unchanged). */
+int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new,
+                  const void* v_new, int32_t n_new, int32_t* len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDL_H */

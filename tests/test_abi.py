@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every declared entry point and validates
+its arguments on the host (no kernel is launched by these checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_decoding_attn_amd import fdl, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fdl.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fdl_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fdl.LIB_PATH):
+        pytest.skip("libfdl.so not built")
+    return fdl.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == set(fdl.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strerror(L):
+    assert fdl.fdl_version() == 100
+    for code in (0, -1, -2, -3, -4):
+        assert fdl.fdl_strerror(code) not in ("", "unknown status")
+    assert fdl.fdl_strerror(7) == "unknown status"
+
+
+def _dims(name="qwen2.5-7b_bs4", **over):
+    d = fdl.make_dims(synth.get_config(name))
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, fdl.FDL_OK),
+    ({"batch": 0}, fdl.FDL_E_INVAL),
+    ({"n_q_heads": 27}, fdl.FDL_E_INVAL),
+    ({"sub_block": 5}, fdl.FDL_E_INVAL),
+    ({"gen_len": 500}, fdl.FDL_E_INVAL),
+    ({"dtype": 7}, fdl.FDL_E_INVAL),
+    ({"attn_mode": 3}, fdl.FDL_E_INVAL),
+    ({"head_dim": 96}, fdl.FDL_E_UNSUPPORTED),
+    ({"prompt_len": -1}, fdl.FDL_E_INVAL),
+])
+def test_dims_check(L, over, code):
+    assert fdl.fdl_dims_check(_dims(**over)) == code
+
+
+def test_workspace_sizes(L):
+    for name in synth.CONFIG_ORDER:
+        cfg = synth.get_config(name)
+        d = fdl.make_dims(cfg)
+        ws = fdl.fdl_block_attn_workspace_size(d)
+        rows = cfg.batch * cfg.n_q_heads * cfg.sub_block
+        assert ws == 0 or ws % (rows * (cfg.head_dim + 2) * 4) == 0
+        assert fdl.fdl_conf_select_workspace_size(d, cfg.sub_block) >= cfg.batch * cfg.sub_block * 16
+    assert fdl.fdl_block_attn_workspace_size(_dims(batch=0)) == 0
+    assert fdl.fdl_conf_select_workspace_size(_dims(), 0) == 0
+    assert fdl.fdl_conf_select_workspace_size(_dims(), 257) == 0
+
+
+def test_entry_points_reject_before_launch(L):
+    """Invalid scalars or null pointers return an error without launching."""
+    d = _dims()
+    P = ctypes.c_void_p
+    fake = P(16)  # never dereferenced: validation fails first
+    by = ctypes.byref
+    # block index out of range, sub index out of range, null pointers
+    assert L.fdl_block_attn(by(d), 16, 0, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -1
+    assert L.fdl_block_attn(by(d), 0, 4, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -1
+    assert L.fdl_block_attn(by(d), 0, 0, None, fake, fake, None, fake, fake, fake, None, None, 0, None) == -1
+    assert L.fdl_block_attn(None, 0, 0, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -1
+    d96 = _dims(head_dim=96)
+    assert L.fdl_block_attn(by(d96), 0, 0, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -2
+    # too many rows per KV head for one workgroup
+    dbig = _dims(n_q_heads=28 * 2, n_kv_heads=2, sub_block=32)
+    assert L.fdl_block_attn(by(dbig), 0, 0, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -2
+    # lm head
+    assert L.fdl_lm_head(by(d), 0, fake, fake, fake, None) == -1
+    assert L.fdl_lm_head(by(d), 4, None, fake, fake, None) == -1
+    assert L.fdl_lm_head(by(_dims(hidden=3600)), 4, fake, fake, fake, None) == -2
+    df = _dims("tiny_fp32")
+    assert L.fdl_lm_head(by(df), 65, fake, fake, fake, None) == -2
+    # select
+    args = [fake, fake, fake, fake]
+    assert L.fdl_conf_select(by(d), 0, fake, fake, fake, 0, 0, 0.0, *args, None, None, fake, 1 << 20, None) == -1
+    assert L.fdl_conf_select(by(d), 8, fake, fake, None, 0, 0, 0.0, *args, None, None, fake, 1 << 20, None) == -1
+    assert L.fdl_conf_select(by(d), 8, fake, fake, fake, 1, 0, 0.0, *args, None, None, fake, 1 << 20, None) == -1
+    assert L.fdl_conf_select(by(d), 8, fake, fake, fake, 2, 0, ctypes.c_float(0.0), *args, None, None, fake,
+                             1 << 20, None) == -1
+    assert L.fdl_conf_select(by(d), 8, fake, fake, fake, 5, 0, 0.0, *args, None, None, fake, 1 << 20, None) == -1
+    # append
+    assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 0, fake, None) == -1
+    assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 1537, fake, None) == -1
+    assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 32, None, None) == -1
