@@ -352,29 +352,47 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of every query row in split order.
+// Merge the split partials of every query row in split order.  Loads are
+// issued eight splits at a time so that their latencies overlap (the partials
+// were written by workgroups on other XCDs and come back from beyond L2).
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void block_attn_merge_kernel(AttnArgs a) {
   constexpr int TPR = DH / 4;  // threads per row, 4 dims each
+  constexpr int U = 8;
   const int n_rows = a.B * a.Hq * a.S;
   const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int d0 = (threadIdx.x % TPR) * 4;
   if (row >= n_rows) return;
   const size_t stride = size_t(n_rows);
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   float mmax = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* ml = a.part_ml + (s * stride + row) * 2;
-    if (ml[1] > 0.f) mmax = fmaxf(mmax, ml[0]);
+  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+    float2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = s0 + u < a.nsplit ? ml[(s0 + u) * stride + row] : float2{-INFINITY, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v[u].y > 0.f) mmax = fmaxf(mmax, v[u].x);
   }
   float lsum = 0.f;
   f32x4 acc{0, 0, 0, 0};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* ml = a.part_ml + (s * stride + row) * 2;
-    if (!(ml[1] > 0.f)) continue;
-    const float w = exp2f(ml[0] - mmax);
-    lsum += w * ml[1];
-    const f32x4 po = *reinterpret_cast<const f32x4*>(a.part_o + (s * stride + row) * DH + d0);
-    acc += w * po;
+  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+    float2 v[U];
+    f32x4 po[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < a.nsplit;
+      v[u] = ok ? ml[(s0 + u) * stride + row] : float2{-INFINITY, 0.f};
+      po[u] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + ((s0 + u) * stride + row) * DH + d0)
+                 : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!(v[u].y > 0.f)) continue;
+      const float w = exp2f(v[u].x - mmax);
+      lsum += w * v[u].y;
+      acc += w * po[u];
+    }
   }
   // row = (b*Hq + h)*S + i  ->  out[b][i][h]
   const int i = row % a.S;

@@ -98,30 +98,45 @@ __global__ __launch_bounds__(256) void select_partial_kernel(SelArgs a) {
   }
 }
 
-// one workgroup per sequence, one thread per row (R <= 256)
+// one workgroup per sequence: each wave merges the chunk partials of rows
+// w, w+4, ... (lanes take chunks lane, lane+64, ... in order, then a fixed
+// butterfly), then one thread per row (R <= 256) applies the selection rule.
 __global__ __launch_bounds__(256) void select_finalize_kernel(SelArgs a) {
   __shared__ float conf_s[256];
+  __shared__ int tok_s[256];
   __shared__ int cand_s[256];
   __shared__ int red_i[256];
   const int b = blockIdx.x, r = threadIdx.x;
-  const bool live = r < a.R;
-  const size_t row = size_t(b) * a.R + r;
-
-  float conf = 0.f;
-  int tok = 0, cand = 0;
-  if (live) {
+  const int lane = r & 63, wave = r >> 6;
+  for (int row_in = wave; row_in < a.R; row_in += 4) {
+    const size_t row = size_t(b) * a.R + row_in;
     Red t{-INFINITY, 0.f, INT_MAX};
-    for (int c = 0; c < a.NC; ++c) {
+    for (int c = lane; c < a.NC; c += 64) {
       const f32x4 p = a.part[row * a.NC + c];
       t = combine(t, Red{p[0], p[1], __float_as_int(p[2])});
     }
-    tok = t.i;
-    conf = 1.f / t.s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      Red u{__shfl_xor(t.m, o, 64), __shfl_xor(t.s, o, 64), __shfl_xor(t.i, o, 64)};
+      t = combine(t, u);
+    }
+    if (lane == 0) {
+      conf_s[row_in] = 1.f / t.s;
+      tok_s[row_in] = t.i;
+    }
+  }
+  __syncthreads();
+  const bool live = r < a.R;
+  const size_t row = size_t(b) * a.R + r;
+  float conf = 0.f;
+  int tok = 0, cand = 0;
+  if (live) {
+    conf = conf_s[r];
+    tok = tok_s[r];
     cand = a.masked[row] != 0;
     a.token_out[row] = tok;
     a.conf_out[row] = conf;
   }
-  conf_s[r] = conf;
   cand_s[r] = live ? cand : 0;
   __syncthreads();
 
