@@ -29,11 +29,17 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "lm_head_qwen2.5-7b_bs4_pmc.txt")
 LM_HEAD_SRC = os.path.join(ROOT, "block_diffusion_decoding_attn_amd", "csrc", "lm_head.hip")
 
 
-def lm_head_bytes_flops(cfg):
-    """Algorithmic bytes and flops of one LM-head launch: W, X read once, logits written once."""
+def lm_head_bytes_flops(cfg, fused: bool):
+    """Algorithmic bytes and flops of one LM-head (+ select) call.
+
+    Unfused fdl_lm_head: W and X read once, the f32 logits written once.
+    Fused fdl_lm_head_select: W and X read once, the select's per-row outputs
+    (token, confidence, commit flag, the in-place token/masked updates) and
+    per-sequence counts written; the logits never exist."""
     esz = 4 if cfg.dtype == "f32" else 2
     M = cfg.rows
-    byts = cfg.vocab * cfg.hidden * esz + M * cfg.hidden * esz + M * cfg.vocab * 4
+    byts = cfg.vocab * cfg.hidden * esz + M * cfg.hidden * esz
+    byts += M * (4 + 4 + 1 + 4 + 1) + cfg.batch * 4 if fused else M * cfg.vocab * 4
     flops = 2.0 * M * cfg.hidden * cfg.vocab
     return byts, flops
 
@@ -106,6 +112,8 @@ def main():
     ap.add_argument("--boost", default="calibrated", choices=["calibrated", "literal"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="fdl_lm_head + fdl_conf_select (logits materialized) instead of fdl_lm_head_select")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -122,7 +130,8 @@ def main():
     fdl.lib()
     cfg = synth.get_config(args.workload)
     t_setup = time.perf_counter()
-    run = StepRunner(cfg, select=args.select, k=args.k, boost=args.boost, keep_host=not args.no_cpu_baseline)
+    run = StepRunner(cfg, select=args.select, k=args.k, boost=args.boost, keep_host=not args.no_cpu_baseline,
+                     fused=not args.unfused)
     print(f"# setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     nsched = len(run.step_ids)
 
@@ -146,10 +155,14 @@ def main():
             run.attention(i)
             if ev is not None:
                 ev[j][0].record()
-            run.lm_head(i)
+            if run.fused:
+                run.lm_head_select(i)
+            else:
+                run.lm_head(i)
             if ev is not None:
                 ev[j][1].record()
-            run.select(i)
+            if not run.fused:
+                run.select(i)
             if inp.append_after and not run.dual:
                 run.append(i)
             pos = (pos + 1) % nsched
@@ -170,7 +183,7 @@ def main():
     committed = sum(commits[(start_pos + j) % nsched] for j in range(args.steps))
     lm_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
-    byts, flops = lm_head_bytes_flops(cfg)
+    byts, flops = lm_head_bytes_flops(cfg, run.fused)
     ai = flops / byts
     if ai > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "mfma", "achieved": flops / (lm_ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
@@ -178,8 +191,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": byts / (lm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = pmc_traffic()
-    roof["kernel"] = "fdl_lm_head"
+    roof["traffic"] = pmc_traffic() if run.fused else None
+    roof["kernel"] = ("fdl_lm_head_select (lm_head_skinny_bf16 with the select epilogue + select_finalize_kernel)"
+                      if run.fused else "fdl_lm_head (lm_head_skinny_bf16)")
     roof["kernel_us"] = lm_ms * 1e3
     roof["algorithmic_bytes"] = byts
 
@@ -200,7 +214,7 @@ def main():
                    "block": cfg.block, "sub_block": cfg.sub_block, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "hidden": cfg.hidden, "vocab": cfg.vocab,
                    "attn_mode": cfg.attn_mode, "select": args.select, "tau": list(cfg.tau), "boost": args.boost,
-                   "parallelism": "single-gpu"},
+                   "lm_head_select": "unfused" if args.unfused else "fused", "parallelism": "single-gpu"},
         "committed_tokens_per_s": committed / (ms * 1e-3),
         "commits_per_step": committed / args.steps,
         "roofline": roof,

@@ -9,7 +9,13 @@ int attn_max_rows();
 int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc, const void* vc,
                 const int32_t* prefix_len, const void* kb, const void* vb, void* out, float* lse, void* ws,
                 size_t ws_bytes, hipStream_t st);
-int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, hipStream_t st);
+int lm_head_tiles(const fdl_dims& d);
+int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
+                   hipStream_t st);
+int select_finalize_launch(const fdl_dims& d, int R, const void* part, int nc, const uint8_t* masked,
+                           const float* tau, int mode, int k, float factor, int32_t* token_out, float* conf_out,
+                           uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
+                           hipStream_t st);
 size_t select_workspace_bytes(const fdl_dims& d, int rows_per_seq);
 int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* masked, const float* tau, int mode,
                   int k, float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out, int32_t* n_commit,
@@ -38,6 +44,32 @@ static int check_dims(const fdl_dims* d) {
   if (cap > (1 << 24) || d->vocab > (1 << 28) || d->hidden > (1 << 20)) return FDL_E_UNSUPPORTED;
   if (d->batch > 65535 || d->n_kv_heads > 32767) return FDL_E_UNSUPPORTED;  // grid y/z extents
   if (d->head_dim != 64 && d->head_dim != 128) return FDL_E_UNSUPPORTED;
+  return FDL_OK;
+}
+
+static int check_select_args(const fdl_dims& d, int32_t rows_per_seq, const uint8_t* masked, const float* tau,
+                             int32_t mode, int32_t k, float factor, const int32_t* token_out, const float* conf_out,
+                             const uint8_t* commit_out, const int32_t* n_commit) {
+  if (rows_per_seq < 1 || rows_per_seq > 256) return FDL_E_INVAL;
+  if (!masked || !token_out || !conf_out || !commit_out || !n_commit) return FDL_E_INVAL;
+  if (mode == FDL_SELECT_THRESHOLD) {
+    if (!tau) return FDL_E_INVAL;
+  } else if (mode == FDL_SELECT_TOPK) {
+    if (k < 1) return FDL_E_INVAL;
+  } else if (mode == FDL_SELECT_FACTOR) {
+    if (!(factor > 0.f)) return FDL_E_INVAL;
+  } else {
+    return FDL_E_INVAL;
+  }
+  if ((long long)d.batch * rows_per_seq > 65535) return FDL_E_UNSUPPORTED;  // grid y extent
+  return FDL_OK;
+}
+
+static int check_lm_head_args(const fdl_dims& d, int32_t rows, const void* x, const void* w) {
+  if (rows < 1 || !x || !w) return FDL_E_INVAL;
+  if (d.dtype == FDL_BF16 && d.hidden % 64 != 0) return FDL_E_UNSUPPORTED;
+  if (d.dtype == FDL_F32 && (d.hidden % 4 != 0 || rows > 64)) return FDL_E_UNSUPPORTED;
+  if ((long long)rows * d.vocab > (1LL << 40)) return FDL_E_UNSUPPORTED;
   return FDL_OK;
 }
 
@@ -86,11 +118,10 @@ int fdl_lm_head(const fdl_dims* dims, int32_t rows, const void* x, const void* w
   int rc = check_dims(dims);
   if (rc != FDL_OK) return rc;
   const fdl_dims& d = *dims;
-  if (rows < 1 || !x || !w || !logits) return FDL_E_INVAL;
-  if (d.dtype == FDL_BF16 && d.hidden % 64 != 0) return FDL_E_UNSUPPORTED;
-  if (d.dtype == FDL_F32 && (d.hidden % 4 != 0 || rows > 64)) return FDL_E_UNSUPPORTED;
-  if ((long long)rows * d.vocab > (1LL << 40)) return FDL_E_UNSUPPORTED;
-  return lm_head_launch(d, rows, x, w, logits, reinterpret_cast<hipStream_t>(stream));
+  if (!logits) return FDL_E_INVAL;
+  rc = check_lm_head_args(d, rows, x, w);
+  if (rc != FDL_OK) return rc;
+  return lm_head_launch(d, rows, x, w, logits, nullptr, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t fdl_conf_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq) {
@@ -105,21 +136,39 @@ int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* log
   int rc = check_dims(dims);
   if (rc != FDL_OK) return rc;
   const fdl_dims& d = *dims;
-  if (rows_per_seq < 1 || rows_per_seq > 256) return FDL_E_INVAL;
-  if (!logits || !masked || !token_out || !conf_out || !commit_out || !n_commit) return FDL_E_INVAL;
-  if (mode == FDL_SELECT_THRESHOLD) {
-    if (!tau) return FDL_E_INVAL;
-  } else if (mode == FDL_SELECT_TOPK) {
-    if (k < 1) return FDL_E_INVAL;
-  } else if (mode == FDL_SELECT_FACTOR) {
-    if (!(factor > 0.f)) return FDL_E_INVAL;
-  } else {
-    return FDL_E_INVAL;
-  }
-  if ((long long)d.batch * rows_per_seq > 65535) return FDL_E_UNSUPPORTED;  // grid y extent
+  if (!logits) return FDL_E_INVAL;
+  rc = check_select_args(d, rows_per_seq, masked, tau, mode, k, factor, token_out, conf_out, commit_out, n_commit);
+  if (rc != FDL_OK) return rc;
   return select_launch(d, rows_per_seq, logits, masked, tau, mode, k, factor, token_out, conf_out, commit_out,
                        n_commit, tokens_inout, masked_inout, workspace, workspace_bytes,
                        reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t fdl_lm_head_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq) {
+  if (check_dims(dims) != FDL_OK || rows_per_seq < 1 || rows_per_seq > 256) return 0;
+  return size_t(dims->batch) * rows_per_seq * lm_head_tiles(*dims) * 16;
+}
+
+int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x, const void* w, float* logits,
+                       const uint8_t* masked, const float* tau, int32_t mode, int32_t k, float factor,
+                       int32_t* token_out, float* conf_out, uint8_t* commit_out, int32_t* n_commit,
+                       int32_t* tokens_inout, uint8_t* masked_inout, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  rc = check_select_args(d, rows_per_seq, masked, tau, mode, k, factor, token_out, conf_out, commit_out, n_commit);
+  if (rc != FDL_OK) return rc;
+  const int rows = d.batch * rows_per_seq;
+  rc = check_lm_head_args(d, rows, x, w);
+  if (rc != FDL_OK) return rc;
+  const int nc = lm_head_tiles(d);
+  if (!workspace || workspace_bytes < size_t(rows) * nc * 16) return FDL_E_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = lm_head_launch(d, rows, x, w, logits, workspace, st);
+  if (rc != FDL_OK) return rc;
+  return select_finalize_launch(d, rows_per_seq, workspace, nc, masked, tau, mode, k, factor, token_out, conf_out,
+                                commit_out, n_commit, tokens_inout, masked_inout, st);
 }
 
 int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new, const void* v_new,

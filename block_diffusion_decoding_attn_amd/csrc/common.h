@@ -61,6 +61,41 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// (max, sum of exp(l - max), lowest argmax) of a run of logits: the partial
+// form of the softmax confidence of one row.
+struct Red {
+  float m, s;
+  int i;
+};
+
+// merge two partials; equal maxima keep the lower index
+__device__ __forceinline__ Red combine(Red a, Red b) {
+  Red r;
+  r.m = fmaxf(a.m, b.m);
+  const float ta = a.s > 0.f ? a.s * exp2f((a.m - r.m) * kLog2e) : 0.f;
+  const float tb = b.s > 0.f ? b.s * exp2f((b.m - r.m) * kLog2e) : 0.f;
+  r.s = ta + tb;
+  r.i = (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b.i : a.i;
+  return r;
+}
+
+__device__ __forceinline__ void push(Red& r, float x, int v) {
+  if (x > r.m) {
+    r.s = r.s * exp2f((r.m - x) * kLog2e) + 1.f;
+    r.m = x;
+    r.i = v;
+  } else {
+    r.s += exp2f((x - r.m) * kLog2e);
+  }
+}
+
+__device__ __forceinline__ f32x4 pack_red(Red r) { return f32x4{r.m, r.s, __int_as_float(r.i), 0.f}; }
+__device__ __forceinline__ Red unpack_red(f32x4 p) { return Red{p[0], p[1], __float_as_int(p[2])}; }
+__device__ __forceinline__ Red red_empty() { return Red{-INFINITY, 0.f, 0x7fffffff}; }
+__device__ __forceinline__ Red shfl_xor_red(Red r, int o) {
+  return Red{__shfl_xor(r.m, o, kWave), __shfl_xor(r.s, o, kWave), __shfl_xor(r.i, o, kWave)};
+}
+
 }  // namespace fdl
 
 // Host-side launch helpers (defined in abi.hip).

@@ -19,9 +19,42 @@ namespace fdl {
 struct LmArgs {
   const void* x;
   const void* w;
-  float* out;
-  int M, H, V;
+  float* out;    // [M][V] logits, or null (fused select: only partials)
+  f32x4* part;   // [M][nc] confidence partials per 128-row vocabulary tile, or null
+  int M, H, V, nc;
 };
+
+// Fused-select epilogue, shared by the skinny kernels: lane holds
+// acc[t][n][e] = logit of vocabulary row vbase + 16t + 4grp + e for column
+// m = 16n + l16.  Reduce each column over the lane's rows (increasing index),
+// then over the 4 lane groups, then over the workgroup's waves through LDS,
+// and write one partial per (row, 128-row vocabulary tile).
+template <int RT, int NTM, int NWAVES>
+__device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (&acc)[RT][NTM], int vbase, int wave,
+                                                  int l16, int grp, int tile, f32x4 (*red)[NTM * 16]) {
+#pragma unroll
+  for (int n = 0; n < NTM; ++n) {
+    Red r = red_empty();
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = vbase + t * 16 + grp * 4 + e;
+        if (v < a.V) push(r, acc[t][n][e], v);
+      }
+    r = combine(r, shfl_xor_red(r, 16));
+    r = combine(r, shfl_xor_red(r, 32));
+    if (grp == 0) red[wave][n * 16 + l16] = pack_red(r);
+  }
+  __syncthreads();
+  const int m = threadIdx.x;
+  if (m < NTM * 16 && m < a.M) {
+    Red r = unpack_red(red[0][m]);
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) r = combine(r, unpack_red(red[w][m]));
+    a.part[size_t(m) * a.nc + tile] = pack_red(r);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // skinny: a workgroup of WPB waves owns ROWS vocabulary rows.  K is walked in
@@ -124,6 +157,11 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
   }
 
   // lane holds C[vocab v0 + wave*RPW + 16t + 4grp + e][m = 16n + l16]
+  if (a.part) {
+    __shared__ f32x4 red[WPB][NTM * 16];
+    epilogue_partials<RT, NTM, WPB>(a, acc, v0 + wave * RPW, wave, l16, grp, blockIdx.x, red);
+  }
+  if (!a.out) return;
 #pragma unroll
   for (int n = 0; n < NTM; ++n) {
     const int m = n * 16 + l16;
@@ -147,11 +185,9 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
 // 16x16x4 f32 MFMA, one k value per lane per instruction.
 template <int NTM, int RT>
 __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int v0 = wave_id * RT * 16;
-  if (v0 >= a.V) return;
+  const int v0 = (blockIdx.x * 4 + wave) * RT * 16;
   const float* W = reinterpret_cast<const float*>(a.w);
   const float* X = reinterpret_cast<const float*>(a.x);
   f32x4 acc[RT][NTM];
@@ -159,22 +195,29 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int n = 0; n < NTM; ++n) acc[t][n] = f32x4{0, 0, 0, 0};
-  for (int k = 0; k < a.H; k += 4) {
-    float xa[NTM];
+  if (v0 < a.V) {
+    for (int k = 0; k < a.H; k += 4) {
+      float xa[NTM];
 #pragma unroll
-    for (int n = 0; n < NTM; ++n) {
-      const int m = n * 16 + l16;
-      xa[n] = m < a.M ? X[size_t(m) * a.H + k + grp] : 0.f;
-    }
+      for (int n = 0; n < NTM; ++n) {
+        const int m = n * 16 + l16;
+        xa[n] = m < a.M ? X[size_t(m) * a.H + k + grp] : 0.f;
+      }
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      int row = v0 + t * 16 + l16;
-      row = row < a.V ? row : a.V - 1;
-      const float wv = W[size_t(row) * a.H + k + grp];
+      for (int t = 0; t < RT; ++t) {
+        int row = v0 + t * 16 + l16;
+        row = row < a.V ? row : a.V - 1;
+        const float wv = W[size_t(row) * a.H + k + grp];
 #pragma unroll
-      for (int n = 0; n < NTM; ++n) acc[t][n] = mfma16x16x4_f32(wv, xa[n], acc[t][n]);
+        for (int n = 0; n < NTM; ++n) acc[t][n] = mfma16x16x4_f32(wv, xa[n], acc[t][n]);
+      }
     }
   }
+  if (a.part) {  // a workgroup covers 4 waves x RT*16 = 128 vocabulary rows when RT = 2
+    __shared__ f32x4 red[4][NTM * 16];
+    epilogue_partials<RT, NTM, 4>(a, acc, v0, wave, l16, grp, blockIdx.x, red);
+  }
+  if (!a.out || v0 >= a.V) return;
 #pragma unroll
   for (int n = 0; n < NTM; ++n) {
     const int m = n * 16 + l16;
@@ -275,6 +318,30 @@ __global__ __launch_bounds__(256) void lm_head_tiled_bf16(LmArgs a) {
     __syncthreads();
   }
   // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile
+  if (a.part) {
+    // per row: over the lane's 32 vocabulary rows (increasing), the other
+    // half-wave, then the two waves sharing the rows
+    __shared__ f32x4 red[2][TB_M];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      Red r = red_empty();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int v = v0 + wv + i * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+          if (v < a.V) push(r, acc[i][j][e], v);
+        }
+      r = combine(r, shfl_xor_red(r, 32));
+      if (half == 0) red[wave & 1][wm + j * 32 + l32] = pack_red(r);
+    }
+    __syncthreads();
+    if (tid < TB_M && m0 + tid < a.M) {
+      const Red r = combine(unpack_red(red[0][tid]), unpack_red(red[1][tid]));
+      a.part[size_t(m0 + tid) * a.nc + vt] = pack_red(r);
+    }
+  }
+  if (!a.out) return;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int m = m0 + wm + j * 32 + l32;
@@ -314,8 +381,11 @@ static void launch_skinny_f32(const LmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((lm_head_skinny_f32<NTM, RT>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
 }
 
-int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, hipStream_t st) {
-  LmArgs a{x, w, logits, rows, d.hidden, d.vocab};
+int lm_head_tiles(const fdl_dims& d) { return (d.vocab + 127) / 128; }
+
+int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
+                   hipStream_t st) {
+  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d)};
   const int ntm = (rows + 15) / 16;
   if (d.dtype == FDL_BF16) {
     switch (ntm) {

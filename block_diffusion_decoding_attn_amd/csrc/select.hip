@@ -37,32 +37,6 @@ struct SelArgs {
   int B, R, V, NC, chunk;
 };
 
-struct Red {
-  float m, s;
-  int i;
-};
-
-// merge two (max, sum of exp relative to max, lowest argmax) triples
-__device__ __forceinline__ Red combine(Red a, Red b) {
-  Red r;
-  r.m = fmaxf(a.m, b.m);
-  const float ta = a.s > 0.f ? a.s * exp2f((a.m - r.m) * kLog2e) : 0.f;
-  const float tb = b.s > 0.f ? b.s * exp2f((b.m - r.m) * kLog2e) : 0.f;
-  r.s = ta + tb;
-  r.i = (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b.i : a.i;
-  return r;
-}
-
-__device__ __forceinline__ void push(Red& r, float x, int v) {
-  if (x > r.m) {
-    r.s = r.s * exp2f((r.m - x) * kLog2e) + 1.f;
-    r.m = x;
-    r.i = v;
-  } else {
-    r.s += exp2f((x - r.m) * kLog2e);
-  }
-}
-
 template <bool VEC>
 __global__ __launch_bounds__(256) void select_partial_kernel(SelArgs a) {
   __shared__ Red sh[4];
@@ -98,34 +72,47 @@ __global__ __launch_bounds__(256) void select_partial_kernel(SelArgs a) {
   }
 }
 
-// one workgroup per sequence: each wave merges the chunk partials of rows
-// w, w+4, ... (lanes take chunks lane, lane+64, ... in order, then a fixed
-// butterfly), then one thread per row (R <= 256) applies the selection rule.
-__global__ __launch_bounds__(256) void select_finalize_kernel(SelArgs a) {
+// One workgroup of 1024 threads per sequence.  Phase 1: the chunk partials
+// of row r are merged by TPR = min(64, 1024 / R') threads (R' = R rounded up
+// to a power of two) that each take chunks j, j+TPR, ... in increasing order,
+// eight independent loads at a time, followed by a fixed butterfly over the
+// TPR lanes.  Phase 2: one thread per row (R <= 256) applies the rule.
+constexpr int FIN_NT = 1024;
+
+__global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   __shared__ float conf_s[256];
   __shared__ int tok_s[256];
   __shared__ int cand_s[256];
   __shared__ int red_i[256];
-  const int b = blockIdx.x, r = threadIdx.x;
-  const int lane = r & 63, wave = r >> 6;
-  for (int row_in = wave; row_in < a.R; row_in += 4) {
-    const size_t row = size_t(b) * a.R + row_in;
-    Red t{-INFINITY, 0.f, INT_MAX};
-    for (int c = lane; c < a.NC; c += 64) {
-      const f32x4 p = a.part[row * a.NC + c];
-      t = combine(t, Red{p[0], p[1], __float_as_int(p[2])});
-    }
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int rpow = 1;
+  while (rpow < a.R) rpow <<= 1;
+  const int tpr = min(64, FIN_NT / rpow);
+  {
+    const int rr = tid / tpr, j = tid % tpr;
+    Red t = red_empty();
+    if (rr < a.R) {
+      const f32x4* prow = a.part + (size_t(b) * a.R + rr) * a.NC;
+      constexpr int U = 8;
+      for (int c0 = j; c0 < a.NC; c0 += tpr * U) {
+        f32x4 p[U];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      Red u{__shfl_xor(t.m, o, 64), __shfl_xor(t.s, o, 64), __shfl_xor(t.i, o, 64)};
-      t = combine(t, u);
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * tpr;
+          p[u] = c < a.NC ? prow[c] : f32x4{-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) t = combine(t, unpack_red(p[u]));
+      }
     }
-    if (lane == 0) {
-      conf_s[row_in] = 1.f / t.s;
-      tok_s[row_in] = t.i;
+    for (int o = 1; o < tpr; o <<= 1) t = combine(t, shfl_xor_red(t, o));
+    if (rr < a.R && j == 0) {
+      conf_s[rr] = 1.f / t.s;
+      tok_s[rr] = t.i;
     }
   }
   __syncthreads();
+  const int r = tid;
   const bool live = r < a.R;
   const size_t row = size_t(b) * a.R + r;
   float conf = 0.f;
@@ -137,7 +124,7 @@ __global__ __launch_bounds__(256) void select_finalize_kernel(SelArgs a) {
     a.token_out[row] = tok;
     a.conf_out[row] = conf;
   }
-  cand_s[r] = live ? cand : 0;
+  if (r < 256) cand_s[r] = live ? cand : 0;
   __syncthreads();
 
   // rank among candidates: decreasing confidence, lower row first on ties
@@ -149,40 +136,45 @@ __global__ __launch_bounds__(256) void select_finalize_kernel(SelArgs a) {
       rank += (cq > conf || (cq == conf && q < r)) ? 1 : 0;
     }
   }
-  bool sel = false;
-  if (a.mode == FDL_SELECT_THRESHOLD) {
-    const float tau = a.tau[b];
-    sel = live && cand && conf > tau;
-    red_i[r] = sel ? 1 : 0;
+  // block reductions over the first 256 threads (every thread reaches each barrier)
+  auto reduce_sum = [&](int v) {
+    if (r < 256) red_i[r] = v;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if (r < o) red_i[r] += red_i[r + o];
       __syncthreads();
     }
-    const int n_above = red_i[0];
+    const int out = red_i[0];
+    __syncthreads();
+    return out;
+  };
+  auto reduce_max = [&](int v) {
+    if (r < 256) red_i[r] = v;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (r < o) red_i[r] = max(red_i[r], red_i[r + o]);
+      __syncthreads();
+    }
+    const int out = red_i[0];
+    __syncthreads();
+    return out;
+  };
+  bool sel = false;
+  if (a.mode == FDL_SELECT_THRESHOLD) {
+    sel = live && cand && conf > a.tau[b];
+    const int n_above = reduce_sum(sel ? 1 : 0);
     if (n_above == 0) sel = live && cand && rank == 0;  // fallback: the most confident candidate
   } else if (a.mode == FDL_SELECT_TOPK) {
     sel = live && cand && rank < a.k;
   } else {  // FDL_SELECT_FACTOR
     const int n = rank + 1;
     const bool ok = live && cand && float(n + 1) * (1.f - conf) < a.factor;
-    red_i[r] = ok ? n : 0;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (r < o) red_i[r] = max(red_i[r], red_i[r + o]);
-      __syncthreads();
-    }
-    const int nstar = red_i[0] > 0 ? red_i[0] : 1;
+    const int best = reduce_max(ok ? n : 0);
+    const int nstar = best > 0 ? best : 1;
     sel = live && cand && rank < nstar;
   }
-  __syncthreads();
-  red_i[r] = sel ? 1 : 0;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (r < o) red_i[r] += red_i[r + o];
-    __syncthreads();
-  }
-  if (r == 0) a.n_commit[b] = red_i[0];
+  const int n_sel = reduce_sum(sel ? 1 : 0);
+  if (r == 0) a.n_commit[b] = n_sel;
   if (live) {
     a.commit_out[row] = sel ? 1 : 0;
     if (sel && a.tokens_inout) a.tokens_inout[row] = tok;
@@ -209,6 +201,23 @@ size_t select_workspace_bytes(const fdl_dims& d, int rows_per_seq) {
   return size_t(d.batch) * rows_per_seq * nc * sizeof(f32x4);
 }
 
+// Finalize from partials produced elsewhere (the LM head's fused epilogue).
+int select_finalize_launch(const fdl_dims& d, int R, const void* part, int nc, const uint8_t* masked,
+                           const float* tau, int mode, int k, float factor, int32_t* token_out, float* conf_out,
+                           uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
+                           hipStream_t st) {
+  SelArgs a;
+  a.logits = nullptr; a.masked = masked; a.tau = tau;
+  a.mode = mode; a.k = k; a.factor = factor;
+  a.token_out = token_out; a.conf_out = conf_out; a.commit_out = commit_out; a.n_commit = n_commit;
+  a.tokens_inout = tokens_inout; a.masked_inout = masked_inout;
+  a.B = d.batch; a.R = R; a.V = d.vocab;
+  a.NC = nc; a.chunk = 0;
+  a.part = reinterpret_cast<f32x4*>(const_cast<void*>(part));
+  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch), dim3(FIN_NT), 0, st, a);
+  return check_launch();
+}
+
 int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* masked, const float* tau, int mode,
                   int k, float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out, int32_t* n_commit,
                   int32_t* tokens_inout, uint8_t* masked_inout, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -225,7 +234,7 @@ int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* 
   const dim3 grid(a.NC, d.batch * R);
   if ((d.vocab & 3) == 0) hipLaunchKernelGGL(select_partial_kernel<true>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(select_partial_kernel<false>, grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch), dim3(FIN_NT), 0, st, a);
   return check_launch();
 }
 

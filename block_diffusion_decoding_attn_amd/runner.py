@@ -34,12 +34,16 @@ class StepRunner:
     """Holds one workload's device state and enqueues its steps.
 
     select: "threshold" (Algorithm 2), "topk" (fixed count `k`) or "factor".
+    fused: LM head and select as one fdl_lm_head_select call (the logits are
+    not materialized unless write_logits); otherwise fdl_lm_head then
+    fdl_conf_select.
     """
 
     def __init__(self, cfg: synth.Config, seed: int = 0, boost: str = "calibrated", select: str = "threshold",
                  k: int = 4, factor: float = 1.0, device: str = "cuda", steps: Optional[List[int]] = None,
-                 keep_host: bool = False):
+                 keep_host: bool = False, fused: bool = True, write_logits: bool = False):
         self.cfg, self.seed, self.boost = cfg, seed, boost
+        self.fused, self.write_logits = fused, write_logits or not fused
         self.select_mode = {"threshold": fdl.FDL_SELECT_THRESHOLD, "topk": fdl.FDL_SELECT_TOPK,
                             "factor": fdl.FDL_SELECT_FACTOR}[select]
         self.k, self.factor = k, factor
@@ -99,7 +103,8 @@ class StepRunner:
         self.n_commit = torch.empty((B,), dtype=torch.int32, device=self.dev)
         self.tokens = torch.zeros((B, S), dtype=torch.int32, device=self.dev)
         ws_a = fdl.fdl_block_attn_workspace_size(self.dims)
-        ws_s = fdl.fdl_conf_select_workspace_size(self.dims, S)
+        ws_s = max(fdl.fdl_conf_select_workspace_size(self.dims, S),
+                   fdl.fdl_lm_head_select_workspace_size(self.dims, S))
         self.ws_attn = torch.empty((max(ws_a, 16),), dtype=torch.uint8, device=self.dev)
         self.ws_sel = torch.empty((max(ws_s, 16),), dtype=torch.uint8, device=self.dev)
 
@@ -130,6 +135,13 @@ class StepRunner:
                             self.k, self.factor, self.token, self.conf, self.commit, self.n_commit, self.tokens,
                             inp.masked, self.ws_sel)
 
+    def lm_head_select(self, i: int):
+        inp = self.inputs[i]
+        fdl.fdl_lm_head_select(self.dims, self.cfg.sub_block, inp.x, self.w,
+                               self.logits if self.write_logits else None, inp.masked, inp.tau, self.select_mode,
+                               self.k, self.factor, self.token, self.conf, self.commit, self.n_commit, self.tokens,
+                               inp.masked, self.ws_sel)
+
     def append(self, i: int):
         b = self.inputs[i].block_idx
         fdl.fdl_kv_append(self.dims, self.k_cache, self.v_cache, self.k_blk[b], self.v_blk[b], self.len)
@@ -139,7 +151,10 @@ class StepRunner:
         if self.dual and inp.sub_idx == 0:
             self.refresh_block(inp.block_idx)
         self.attention(i)
-        self.lm_head(i)
-        self.select(i)
+        if self.fused:
+            self.lm_head_select(i)
+        else:
+            self.lm_head(i)
+            self.select(i)
         if inp.append_after and not self.dual:
             self.append(i)

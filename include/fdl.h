@@ -9,6 +9,8 @@
  *   fdl_lm_head      hidden rows -> vocabulary logits
  *   fdl_conf_select  greedy token, confidence, commit set per sequence
  *   fdl_kv_append    append a finished block's K/V to the cache
+ * fdl_lm_head_select runs the second and third as one pass that never
+ * materializes the logits.
  *
  * Pages defining the operations (cited by title and section):
  *   "Fast-dLLM v2: Efficient Block-Diffusion LLM" (technical breakdown):
@@ -85,7 +87,8 @@ typedef enum {
  *               block % sub_block == 0
  *   n_q_heads   Hq; n_kv_heads Hkv divides Hq (query head h reads KV head h / (Hq/Hkv))
  *   head_dim    d, 64 or 128
- *   hidden      H, LM-head input width (a multiple of 32 for bf16, of 4 for f32)
+ *   hidden      H, LM-head input width (a multiple of 64 for bf16, of 4 for f32;
+ *               f32 LM heads take at most 64 rows)
  *   vocab       V
  *   dtype       fdl_dtype of Q/K/V/O, X and W
  *   attn_mode   fdl_attn_mode
@@ -176,6 +179,28 @@ int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* log
                     float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out,
                     int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fdl_lm_head_select needs: 16 bytes per (row,
+ * 128-row vocabulary tile).  0 for invalid arguments. */
+size_t fdl_lm_head_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq);
+
+/* LM head fused with the confidence select: the same results as fdl_lm_head
+ * followed by fdl_conf_select on its logits, but the LM head's epilogue
+ * reduces every (row, 128-row vocabulary tile) of logits it computes to the
+ * select's (max, lowest argmax, sum exp) partial, so the B*R*V f32 logits are
+ * neither written nor read back ("Fast-dLLM v2", Level 2: only the argmax and
+ * its probability are consumed).  Arguments as in fdl_lm_head (rows =
+ * B * rows_per_seq) and fdl_conf_select, except:
+ *   logits     [B*R][V] f32, or NULL to skip writing them
+ *   workspace  >= fdl_lm_head_select_workspace_size(dims, rows_per_seq) bytes
+ * Confidences may differ from the unfused path in the last bits (the partial
+ * sums are formed in a different order). */
+int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x, const void* w,
+                       float* logits, const uint8_t* masked, const float* tau, int32_t mode,
+                       int32_t k, float factor, int32_t* token_out, float* conf_out,
+                       uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout,
+                       uint8_t* masked_inout, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* KV append ("Fast-dLLM v2", Level 3 block-level cache: a finished block's
  * K/V are stored for all later steps; Fast-dLLM Algorithm 1: the refresh

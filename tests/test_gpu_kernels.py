@@ -223,3 +223,61 @@ def test_kv_append_bitwise(kw, lens, n_new):
         ok_k, ok_l = O.kv_append(kc.float().numpy(), kn.float().numpy(), ln.numpy())
         np.testing.assert_array_equal(kg.float().numpy(), ok_k)
         assert lg.tolist() == ok_l.tolist()
+
+
+@pytest.mark.parametrize("B,R,H,V,dtype,mode", [
+    (4, 8, 512, 1000, "bf16", O.SELECT_THRESHOLD),      # V not a multiple of the 128-row tile
+    (1, 8, 256, 4096, "bf16", O.SELECT_TOPK),
+    (2, 32, 512, 2003, "bf16", O.SELECT_FACTOR),        # M = 64
+    (5, 32, 256, 1000, "bf16", O.SELECT_THRESHOLD),     # M = 160: tiled kernel
+    (1, 32, 256, 512, "f32", O.SELECT_THRESHOLD),
+    (2, 8, 260, 77, "f32", O.SELECT_TOPK),
+])
+def test_lm_head_select_parity(B, R, H, V, dtype, mode):
+    """Fused LM head + select against the oracle (logits in fp64, select on
+    them) and against the unfused GPU path on the same inputs."""
+    dev = _dev()
+    cfg = _cfg(batch=B, sub_block=R, block=R, gen_len=R, hidden=H, vocab=V, dtype=dtype)
+    d = fdl.make_dims(cfg)
+    w = synth.weights(cfg)
+    x, _, _ = synth.hidden_rows(cfg, w, 3)
+    rng = np.random.default_rng(B * R + V)
+    masked = torch.as_tensor((rng.random((B, R)) < 0.8).astype(np.uint8))
+    masked[0, 0] = 1
+    tau = torch.as_tensor(rng.choice([0.5, 0.7, 0.9], B).astype(np.float32))
+    gmode = {O.SELECT_THRESHOLD: 0, O.SELECT_TOPK: 1, O.SELECT_FACTOR: 2}[mode]
+
+    def outs():
+        return dict(token=torch.empty((B, R), dtype=torch.int32, device=dev),
+                    conf=torch.empty((B, R), dtype=torch.float32, device=dev),
+                    commit=torch.empty((B, R), dtype=torch.uint8, device=dev),
+                    n_commit=torch.empty((B,), dtype=torch.int32, device=dev))
+    xd, wd, md, td = x.to(dev), w.to(dev), masked.to(dev), tau.to(dev)
+    fused, unfused = outs(), outs()
+    lg_f = torch.empty((B * R, V), dtype=torch.float32, device=dev)
+    lg_u = torch.empty((B * R, V), dtype=torch.float32, device=dev)
+    ws = torch.empty((fdl.fdl_lm_head_select_workspace_size(d, R),), dtype=torch.uint8, device=dev)
+    fdl.fdl_lm_head_select(d, R, xd, wd, lg_f, md, td, gmode, 3, 1.5, fused["token"], fused["conf"],
+                           fused["commit"], fused["n_commit"], None, None, ws)
+    fused2 = outs()
+    fdl.fdl_lm_head_select(d, R, xd, wd, None, md, td, gmode, 3, 1.5, fused2["token"], fused2["conf"],
+                           fused2["commit"], fused2["n_commit"], None, None, ws)
+    fdl.fdl_lm_head(d, xd, wd, lg_u)
+    ws2 = torch.empty((fdl.fdl_conf_select_workspace_size(d, R),), dtype=torch.uint8, device=dev)
+    fdl.fdl_conf_select(d, R, lg_u, md, td, gmode, 3, 1.5, unfused["token"], unfused["conf"], unfused["commit"],
+                        unfused["n_commit"], None, None, ws2)
+    torch.cuda.synchronize()
+    # logits written by the fused call are the LM head's, bit for bit
+    assert torch.equal(lg_f, lg_u)
+    got = {k_: v.cpu().numpy() for k_, v in fused.items()}
+    got2 = {k_: v.cpu().numpy() for k_, v in fused2.items()}
+    for k_ in got:
+        np.testing.assert_array_equal(got[k_], got2[k_])       # writing logits or not changes nothing
+    gu = {k_: v.cpu().numpy() for k_, v in unfused.items()}
+    np.testing.assert_array_equal(got["token"], gu["token"])   # same fp32 logits: same argmax
+    np.testing.assert_allclose(got["conf"], gu["conf"], rtol=1e-5)
+    ref_logits = O.lm_head(x, w)
+    assert normwise(lg_f.cpu().numpy(), ref_logits) <= (1e-5 if dtype == "f32" else 1e-4)
+    ref = O.conf_select(ref_logits.reshape(B, R, V), masked.numpy(), tau.numpy(), mode, 3, 1.5)
+    st = compare_select(ref, got, masked.numpy(), tau.numpy(), mode, 3, 1.5, eps=1e-3)
+    assert st["seq_checked"] + st["seq_excluded"] == B

@@ -106,7 +106,7 @@ def _check_step(run: StepRunner, i: int, seqs, groups, vocab_sample=2048, select
 def test_tiny_fp32_step_exact_sizes():
     _need_gpu()
     cfg = synth.get_config("tiny_fp32")
-    run = StepRunner(cfg, keep_host=True)
+    run = StepRunner(cfg, keep_host=True, write_logits=True)
     st = _check_step(run, 0, seqs=[0], groups=[0, 1], vocab_sample=512)
     assert st["seq_checked"] == 1
     # whole attention output and logits at this size
@@ -118,23 +118,26 @@ def test_tiny_fp32_step_exact_sizes():
     assert normwise(run.out.cpu().numpy(), ref_o) <= 1e-5
 
 
-@pytest.mark.parametrize("name,steps,seqs,groups,select", [
-    ("qwen2.5-1.5b_bs1", [0, 3, 31], [0], [0, 1], "threshold"),
-    ("qwen2.5-7b_bs4", [0, 63], [0, 3], [0, 3], "threshold"),
-    ("qwen2.5-7b_bs4", [5], [1, 2], [1], "topk"),
-    ("llada-8b_dualcache", [0, 31], [0], [0, 17, 31], "threshold"),
-    ("qwen2.5-7b_long_bs16", [0], [0, 9], [0, 2], "threshold"),
-    ("qwen2.5-7b_long_bs16", [0], [4], [1], "factor"),
+@pytest.mark.parametrize("name,steps,seqs,groups,select,fused", [
+    ("qwen2.5-1.5b_bs1", [0, 3, 31], [0], [0, 1], "threshold", True),
+    ("qwen2.5-7b_bs4", [0, 63], [0, 3], [0, 3], "threshold", True),
+    ("qwen2.5-7b_bs4", [2, 3], [1, 2], [1, 2], "threshold", False),
+    ("qwen2.5-7b_bs4", [5], [1, 2], [1], "topk", True),
+    ("llada-8b_dualcache", [0, 31], [0], [0, 17, 31], "threshold", True),
+    ("qwen2.5-7b_long_bs16", [0], [0, 9], [0, 2], "threshold", True),
+    ("qwen2.5-7b_long_bs16", [0], [3, 12], [3], "threshold", False),
+    ("qwen2.5-7b_long_bs16", [0], [4], [1], "factor", True),
 ])
-def test_workload_step_parity(name, steps, seqs, groups, select):
+def test_workload_step_parity(name, steps, seqs, groups, select, fused):
     _need_gpu()
     cfg = synth.get_config(name)
-    run = StepRunner(cfg, steps=steps, keep_host=True, select=select, k=4, factor=1.0)
+    run = StepRunner(cfg, steps=steps, keep_host=True, select=select, k=4, factor=1.0, fused=fused,
+                     write_logits=True)
     total = dict(seq_checked=0, seq_excluded=0, token_checked=0, token_excluded=0)
     for i in steps:
         st = _check_step(run, i, seqs, groups, select=select, k=4, factor=1.0)
         for key in total:
             total[key] += st[key]
-    print(name, select, total)
+    print(name, select, "fused" if fused else "unfused", total)
     assert total["seq_checked"] >= 1
     assert total["token_checked"] >= 1
