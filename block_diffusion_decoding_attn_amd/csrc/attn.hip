@@ -99,8 +99,8 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
   constexpr int VST = TK + VPAD;
   constexpr int DT = DH / 16;                  // 16-row tiles of the head dim
 
-  __shared__ __attribute__((aligned(16))) T Ks[TK * KST];
-  __shared__ __attribute__((aligned(16))) T Vt[DH * VST];
+  __shared__ __attribute__((aligned(16))) T Ks[2][TK * KST];
+  __shared__ __attribute__((aligned(16))) T Vt[2][DH * VST];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,16 +170,21 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
     return cache + size_t(j) * DH;
   };
 
-  u32x4 kreg[KCH_T];
-  u32x4 vreg[VU_T][4];
-  auto load_tile = [&](int key0) {
+  // one register stage and two LDS buffers: tile t+1 is in flight while
+  // tile t is consumed from LDS; one barrier per tile
+  struct Stage {
+    u32x4 k[KCH_T];
+    u32x4 v[VU_T][4];
+  };
+  Stage st0;
+  auto load_tile = [&](Stage& S_, int key0) {
 #pragma unroll
     for (int c = 0; c < KCH_T; ++c) {
       const int ch = tid + c * NT;
-      kreg[c] = u32x4{0, 0, 0, 0};
+      S_.k[c] = u32x4{0, 0, 0, 0};
       if (ch < KCH) {
         const int key = key0 + ch / CPR;
-        if (key < k_end) kreg[c] = ld16(key_ptr(kc, kbk, key) + (ch % CPR) * EPC);
+        if (key < k_end) S_.k[c] = ld16(key_ptr(kc, kbk, key) + (ch % CPR) * EPC);
       }
     }
 #pragma unroll
@@ -187,19 +192,19 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
       const int un = tid + u * NT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vreg[u][e] = u32x4{0, 0, 0, 0};
+        S_.v[u][e] = u32x4{0, 0, 0, 0};
         if (un < VU) {
           const int key = key0 + (un % (TK / 4)) * 4 + e;
-          if (key < k_end) vreg[u][e] = ld16(key_ptr(vc, vbk, key) + (un / (TK / 4)) * EPC);
+          if (key < k_end) S_.v[u][e] = ld16(key_ptr(vc, vbk, key) + (un / (TK / 4)) * EPC);
         }
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const Stage& S_, int buf) {
 #pragma unroll
     for (int c = 0; c < KCH_T; ++c) {
       const int ch = tid + c * NT;
-      if (ch < KCH) *reinterpret_cast<u32x4*>(&Ks[(ch / CPR) * KST + (ch % CPR) * EPC]) = kreg[c];
+      if (ch < KCH) *reinterpret_cast<u32x4*>(&Ks[buf][(ch / CPR) * KST + (ch % CPR) * EPC]) = S_.k[c];
     }
 #pragma unroll
     for (int u = 0; u < VU_T; ++u) {
@@ -209,120 +214,125 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
       const int d0 = (un / (TK / 4)) * EPC;
       if constexpr (sizeof(T) == 2) {
         // 4 keys x 8 dims -> 8 rows of V^T, 4 contiguous keys (8 bytes) each
-        const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&vreg[u][0]);
-        const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&vreg[u][1]);
-        const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&vreg[u][2]);
-        const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&vreg[u][3]);
+        const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&S_.v[u][0]);
+        const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&S_.v[u][1]);
+        const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&S_.v[u][2]);
+        const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&S_.v[u][3]);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           u32x2 w;
           w[0] = uint32_t(e0[x]) | (uint32_t(e1[x]) << 16);
           w[1] = uint32_t(e2[x]) | (uint32_t(e3[x]) << 16);
-          *reinterpret_cast<u32x2*>(&Vt[(d0 + x) * VST + k4]) = w;
+          *reinterpret_cast<u32x2*>(&Vt[buf][(d0 + x) * VST + k4]) = w;
         }
       } else {
         // 4 keys x 4 dims -> 4 rows of V^T, 4 contiguous keys (16 bytes) each
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          u32x4 w{vreg[u][0][x], vreg[u][1][x], vreg[u][2][x], vreg[u][3][x]};
-          *reinterpret_cast<u32x4*>(&Vt[(d0 + x) * VST + k4]) = w;
+          u32x4 w{S_.v[u][0][x], S_.v[u][1][x], S_.v[u][2][x], S_.v[u][3][x]};
+          *reinterpret_cast<u32x4*>(&Vt[buf][(d0 + x) * VST + k4]) = w;
         }
       }
     }
   };
 
-  const int ntiles = (k_end - k_begin + TK - 1) / TK;
-  load_tile(k_begin);
-  for (int t = 0; t < ntiles; ++t) {
-    const int key0 = k_begin + t * TK;
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(key0 + TK);
-
-    // ---- S^T = K Q^T : s[j][kt] holds keys key0 + 16kt + 4grp + v for query column l16
-    f32x4 s[RB][4];
+  auto compute_tile = [&](int buf, int key0) {
+      // ---- S^T = K Q^T : s[j][kt] holds keys key0 + 16kt + 4grp + v for query column l16
+      f32x4 s[RB][4];
 #pragma unroll
-    for (int j = 0; j < RB; ++j)
+      for (int j = 0; j < RB; ++j)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) s[j][kt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < 4; ++kt) s[j][kt] = f32x4{0, 0, 0, 0};
+      // k-steps outermost so that consecutive MFMAs feed independent accumulators
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const typename F::type kf = F::load(&Ks[(kt * 16 + l16) * KST + ks * F::KPI + F::EPL * grp]);
 #pragma unroll
-        for (int j = 0; j < RB; ++j) s[j][kt] = F::mma(kf, qf[j][ks], s[j][kt]);
-      }
-    }
-
-    const bool partial = key0 + TK > k_end;
+        for (int kt = 0; kt < 4; ++kt) {
+          const typename F::type kf = F::load(&Ks[buf][(kt * 16 + l16) * KST + ks * F::KPI + F::EPL * grp]);
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float x = s[j][kt][v] * a.scale_log2;
-          if (partial && key0 + kt * 16 + grp * 4 + v >= k_end) x = -INFINITY;
-          s[j][kt][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m[j], mx);
-      const float alpha = exp2f(m[j] - mn);
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = exp2f(s[j][kt][v] - mn);
-          s[j][kt][v] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l[j] = l[j] * alpha + rs;
-      m[j] = mn;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[j][dt] *= alpha;
-    }
-
-    // ---- O^T += V^T P^T
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int c = 0; c < TK / 32; ++c) {
-        u32x4 pf[RB];
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          pf[j][0] = pack_bf16x2(s[j][2 * c][0], s[j][2 * c][1]);
-          pf[j][1] = pack_bf16x2(s[j][2 * c][2], s[j][2 * c][3]);
-          pf[j][2] = pack_bf16x2(s[j][2 * c + 1][0], s[j][2 * c + 1][1]);
-          pf[j][3] = pack_bf16x2(s[j][2 * c + 1][2], s[j][2 * c + 1][3]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const T* row = &Vt[(dt * 16 + l16) * VST + c * 32 + grp * 4];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-          const u32x4 vf{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int j = 0; j < RB; ++j) o[j][dt] = mfma16x16x32_bf16(vf, pf[j], o[j][dt]);
+          for (int j = 0; j < RB; ++j) s[j][kt] = F::mma(kf, qf[j][ks], s[j][kt]);
         }
       }
-    } else {
+
+      const bool partial = key0 + TK > k_end;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int j = 0; j < RB; ++j) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float x = s[j][kt][v] * a.scale_log2;
+            if (partial && key0 + kt * 16 + grp * 4 + v >= k_end) x = -INFINITY;
+            s[j][kt][v] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[j], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - mn);
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s[j][kt][v] - mn);
+            s[j][kt][v] = p;
+            rs += p;
+          }
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        l[j] = l[j] * alpha + rs;
+        m[j] = mn;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[j][dt] *= alpha;
+      }
+
+      // ---- O^T += V^T P^T
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c = 0; c < TK / 32; ++c) {
+          u32x4 pf[RB];
+#pragma unroll
+          for (int j = 0; j < RB; ++j) {
+            pf[j][0] = pack_bf16x2(s[j][2 * c][0], s[j][2 * c][1]);
+            pf[j][1] = pack_bf16x2(s[j][2 * c][2], s[j][2 * c][3]);
+            pf[j][2] = pack_bf16x2(s[j][2 * c + 1][0], s[j][2 * c + 1][1]);
+            pf[j][3] = pack_bf16x2(s[j][2 * c + 1][2], s[j][2 * c + 1][3]);
+          }
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const float vf = reinterpret_cast<const float*>(Vt)[(dt * 16 + l16) * VST + kt * 16 + grp * 4 + v];
+            const T* row = &Vt[buf][(dt * 16 + l16) * VST + c * 32 + grp * 4];
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+            const u32x4 vf{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-            for (int j = 0; j < RB; ++j) o[j][dt] = mfma16x16x4_f32(vf, s[j][kt][v], o[j][dt]);
+            for (int j = 0; j < RB; ++j) o[j][dt] = mfma16x16x32_bf16(vf, pf[j], o[j][dt]);
           }
-    }
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+              const float vf = reinterpret_cast<const float*>(Vt[buf])[(dt * 16 + l16) * VST + kt * 16 + grp * 4 + v];
+#pragma unroll
+              for (int j = 0; j < RB; ++j) o[j][dt] = mfma16x16x4_f32(vf, s[j][kt][v], o[j][dt]);
+            }
+      }
+  };
+
+  const int ntiles = (k_end - k_begin + TK - 1) / TK;
+  load_tile(st0, k_begin);
+  store_tile(st0, 0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(st0, k_begin + (t + 1) * TK);
+    compute_tile(buf, k_begin + t * TK);
+    if (t + 1 < ntiles) store_tile(st0, buf ^ 1);
     __syncthreads();
   }
 
