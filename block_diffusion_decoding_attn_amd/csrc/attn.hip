@@ -82,6 +82,7 @@ __device__ __forceinline__ void store4(float* p, f32x4 v, float s) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0] * s, v[1] * s, v[2] * s, v[3] * s};
 }
 
+// f32 data (and the generic 16-row layout): 16x16x4 f32 MFMA.
 template <typename T, int DH, int NW, int RB>
 __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
   typedef Frag<T> F;
@@ -362,6 +363,268 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
   }
 }
 
+// bf16 data: 32x32x16 MFMA (on gfx950 twice the rate of 16x16x32).  Each of
+// the NW waves owns 32 query rows (NW*32 >= G*S); every wave helps stage the
+// K/V tiles.  S^T = K Q^T leaves a lane with 32 scores of its query column
+// (lane & 31): keys key0 + 32kt + 8(v/4) + 4h + v%4, h = lane >> 5.  Packed
+// 16 at a time, those are exactly the B operand of O^T += V^T P^T under the
+// k permutation {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk, which the V^T
+// fragments read with the same permutation.  Row statistics need one
+// cross-lane exchange (lane ^ 32).  The running maximum is only moved when a
+// tile raises it by more than 2^8 (log2 units 8): p then stays below 256, the
+// normalization is unchanged, and the O/l rescale is skipped on most tiles.
+template <int DH, int NW>
+__global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
+  constexpr int RB = 1;
+  constexpr int KSTEPS = DH / 16, DT = DH / 32;
+  typedef bf16_t T;
+  constexpr int NT = NW * 64;
+  constexpr int EPC = 8, CPR = DH / EPC;
+  constexpr int KCH = TK * CPR, KCH_T = (KCH + NT - 1) / NT;
+  constexpr int VU = (TK / 4) * CPR, VU_T = (VU + NT - 1) / NT;
+  constexpr int KST = DH + 8;   // 272 B rows
+  constexpr int VST = TK + 4;   // 136 B rows
+  __shared__ __attribute__((aligned(16))) T Ks[2][TK * KST];
+  __shared__ __attribute__((aligned(16))) T Vt[2][DH * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+
+  int lp = a.default_lp;
+  if (a.prefix_len) {
+    lp = a.prefix_len[b];
+    lp = lp < 0 ? 0 : (lp > a.cap - a.D ? a.cap - a.D : lp);
+  }
+  const int lk = a.dual ? a.cap : lp + a.D;
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(k_begin + a.split_keys, lk);
+  const int rows = a.G * a.S;
+  constexpr int row0 = 0, rows_per_rg = NW * RB * 32;
+  const size_t pair = size_t(b) * a.Hkv + g;
+  const T* kc = reinterpret_cast<const T*>(a.kc) + pair * a.cap * DH;
+  const T* vc = reinterpret_cast<const T*>(a.vc) + pair * a.cap * DH;
+  const T* kbk = reinterpret_cast<const T*>(a.kb) + pair * a.D * DH;
+  const T* vbk = reinterpret_cast<const T*>(a.vb) + pair * a.D * DH;
+
+  if (k_begin >= lk) {
+    for (int r = row0 + tid; r < min(rows, row0 + rows_per_rg); r += NT) {
+      const int hq = g * a.G + r / a.S, i = r % a.S;
+      const size_t row = (size_t(b) * a.Hq + hq) * a.S + i;
+      float* ml = a.part_ml + (size_t(split) * a.B * a.Hq * a.S + row) * 2;
+      ml[0] = -INFINITY;
+      ml[1] = 0.f;
+    }
+    return;
+  }
+
+  u32x4 qf[RB][KSTEPS];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int r = row0 + (wave + NW * j) * 32 + l32;
+    const bool ok = r < rows;
+    const T* qp = nullptr;
+    if (ok) {
+      const int hq = g * a.G + r / a.S, i = r % a.S;
+      qp = reinterpret_cast<const T*>(a.q) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[j][ks] = ok ? ld16(qp + ks * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+  f32x16 o[RB][DT];
+  float m[RB], l[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[j][dt][e] = 0.f;
+  }
+  auto key_ptr = [&](const T* cache, const T* blk, int j) -> const T* {
+    if (j >= lp && j < lp + a.D) return blk + size_t(j - lp) * DH;
+    return cache + size_t(j) * DH;
+  };
+  u32x4 kreg[KCH_T];
+  u32x4 vreg[VU_T][4];
+  auto load_tile = [&](int key0) {
+#pragma unroll
+    for (int c = 0; c < KCH_T; ++c) {
+      const int ch = tid + c * NT;
+      kreg[c] = u32x4{0, 0, 0, 0};
+      if (ch < KCH) {
+        const int key = key0 + ch / CPR;
+        if (key < k_end) kreg[c] = ld16(key_ptr(kc, kbk, key) + (ch % CPR) * EPC);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VU_T; ++u) {
+      const int un = tid + u * NT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vreg[u][e] = u32x4{0, 0, 0, 0};
+        if (un < VU) {
+          const int key = key0 + (un % (TK / 4)) * 4 + e;
+          if (key < k_end) vreg[u][e] = ld16(key_ptr(vc, vbk, key) + (un / (TK / 4)) * EPC);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < KCH_T; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < KCH) *reinterpret_cast<u32x4*>(&Ks[buf][(ch / CPR) * KST + (ch % CPR) * EPC]) = kreg[c];
+    }
+#pragma unroll
+    for (int u = 0; u < VU_T; ++u) {
+      const int un = tid + u * NT;
+      if (un >= VU) continue;
+      const int k4 = (un % (TK / 4)) * 4;
+      const int d0 = (un / (TK / 4)) * EPC;
+      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&vreg[u][0]);
+      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&vreg[u][1]);
+      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&vreg[u][2]);
+      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&vreg[u][3]);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        u32x2 w;
+        w[0] = uint32_t(e0[x]) | (uint32_t(e1[x]) << 16);
+        w[1] = uint32_t(e2[x]) | (uint32_t(e3[x]) << 16);
+        *reinterpret_cast<u32x2*>(&Vt[buf][(d0 + x) * VST + k4]) = w;
+      }
+    }
+  };
+  auto compute_tile = [&](int buf, int key0) {
+    // S^T = K Q^T: s[j][kt][v] = score of key key0 + 32kt + 8(v/4) + 4h + v%4, query column l32
+    f32x16 s[RB][2];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[j][kt][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(&Ks[buf][(kt * 32 + l32) * KST + ks * 16 + 8 * h]);
+#pragma unroll
+        for (int j = 0; j < RB; ++j) s[j][kt] = mfma32x32x16_bf16(kf, qf[j][ks], s[j][kt]);
+      }
+    }
+    const bool partial = key0 + TK > k_end;
+    const float c = a.scale_log2;
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      if (partial) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (key0 + kt * 32 + (v / 4) * 8 + h * 4 + (v % 4) >= k_end) s[j][kt][v] = -INFINITY;
+      }
+      float mx = s[j][0][0];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][kt][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      // lazy rescale: keep the running reference unless the new maximum
+      // exceeds it by more than 8 (log2 units); p then stays below 2^8
+      if (__builtin_amdgcn_ballot_w64(mx > m[j] + 8.f) != 0) {
+        const float mn = fmaxf(m[j], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - mn);
+        l[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[j][dt] *= alpha;
+        m[j] = mn;
+      }
+      float rs = 0.f;
+      const float mneg = -m[j];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[j][kt][v], c, mneg));
+          s[j][kt][v] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l[j] += rs;
+    }
+    // O^T += V^T P^T over 16-key chunks (kt, q)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        u32x4 pf[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          pf[j][0] = pack_bf16x2(s[j][kt][8 * q + 0], s[j][kt][8 * q + 1]);
+          pf[j][1] = pack_bf16x2(s[j][kt][8 * q + 2], s[j][kt][8 * q + 3]);
+          pf[j][2] = pack_bf16x2(s[j][kt][8 * q + 4], s[j][kt][8 * q + 5]);
+          pf[j][3] = pack_bf16x2(s[j][kt][8 * q + 6], s[j][kt][8 * q + 7]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const T* row = &Vt[buf][(dt * 32 + l32) * VST + kt * 32 + q * 16 + h * 4];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
+          const u32x4 vf{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int j = 0; j < RB; ++j) o[j][dt] = mfma32x32x16_bf16(vf, pf[j], o[j][dt]);
+        }
+      }
+  };
+
+  const int ntiles = (k_end - k_begin + TK - 1) / TK;
+  load_tile(k_begin);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(k_begin + (t + 1) * TK);
+    compute_tile(buf, k_begin + t * TK);
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  // epilogue: o[j][dt][v] = O^T[d = 32dt + 8(v/4) + 4h + v%4][query l32]
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int r = row0 + (wave + NW * j) * 32 + l32;
+    if (r >= rows) continue;
+    const int hq = g * a.G + r / a.S, i = r % a.S;
+    const size_t row = (size_t(b) * a.Hq + hq) * a.S + i;
+    if (a.nsplit == 1) {
+      const float inv = 1.f / l[j];
+      T* op = reinterpret_cast<T*>(a.out) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          store4(op + dt * 32 + q4 * 8 + h * 4,
+                 f32x4{o[j][dt][4 * q4], o[j][dt][4 * q4 + 1], o[j][dt][4 * q4 + 2], o[j][dt][4 * q4 + 3]}, inv);
+      if (a.lse && h == 0) a.lse[row] = (m[j] + __log2f(l[j])) * kLn2;
+    } else {
+      float* po = a.part_o + (size_t(split) * a.B * a.Hq * a.S + row) * DH;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          store4(po + dt * 32 + q4 * 8 + h * 4,
+                 f32x4{o[j][dt][4 * q4], o[j][dt][4 * q4 + 1], o[j][dt][4 * q4 + 2], o[j][dt][4 * q4 + 3]}, 1.f);
+      if (h == 0) {
+        float* ml = a.part_ml + (size_t(split) * a.B * a.Hq * a.S + row) * 2;
+        ml[0] = m[j];
+        ml[1] = l[j];
+      }
+    }
+  }
+}
+
+
 // Merge the split partials of every query row in split order.  Loads are
 // issued eight splits at a time so that their latencies overlap (the partials
 // were written by workgroups on other XCDs and come back from beyond L2).
@@ -425,7 +688,8 @@ static int n_row_blocks(const fdl_dims& d) { return (d.n_q_heads / d.n_kv_heads 
 static AttnPlan plan_for(const fdl_dims& d, int lk) {
   AttnPlan p;
   const int nrb = n_row_blocks(d);
-  if (nrb <= 1) p.nw = 1, p.rb = 1;
+  if (d.dtype == FDL_BF16) p.nw = nrb <= 8 ? 4 : 8, p.rb = 1;   // 32-row blocks, <= 128 / 256 rows
+  else if (nrb <= 1) p.nw = 1, p.rb = 1;
   else if (nrb <= 2) p.nw = 2, p.rb = 1;
   else if (nrb <= 4) p.nw = 4, p.rb = 1;
   else if (nrb <= 8) p.nw = 8, p.rb = 1;
@@ -466,19 +730,30 @@ static void launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
 }
 
 template <typename T, int DH>
-static void launch_attn_cfg(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
+static void launch_merge(const AttnArgs& a, hipStream_t st) {
+  const int n_rows = a.B * a.Hq * a.S;
+  const int rows_per_block = 256 / (DH / 4);
+  hipLaunchKernelGGL((block_attn_merge_kernel<T, DH>), dim3((n_rows + rows_per_block - 1) / rows_per_block),
+                     dim3(256), 0, st, a);
+}
+
+template <int DH>
+static void launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   dim3 grid(p.nsplit, a.Hkv, a.B);
-  if (p.rb == 2) launch_attn<T, DH, 8, 2>(a, grid, st);
-  else if (p.nw == 8) launch_attn<T, DH, 8, 1>(a, grid, st);
-  else if (p.nw == 4) launch_attn<T, DH, 4, 1>(a, grid, st);
-  else if (p.nw == 2) launch_attn<T, DH, 2, 1>(a, grid, st);
-  else launch_attn<T, DH, 1, 1>(a, grid, st);
-  if (p.nsplit > 1) {
-    const int n_rows = a.B * a.Hq * a.S;
-    const int rows_per_block = 256 / (DH / 4);
-    hipLaunchKernelGGL((block_attn_merge_kernel<T, DH>), dim3((n_rows + rows_per_block - 1) / rows_per_block),
-                       dim3(256), 0, st, a);
-  }
+  if (p.nw == 8) hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 8>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 4>), grid, dim3(256), 0, st, a);
+  if (p.nsplit > 1) launch_merge<bf16_t, DH>(a, st);
+}
+
+template <int DH>
+static void launch_attn_f32(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
+  dim3 grid(p.nsplit, a.Hkv, a.B);
+  if (p.rb == 2) launch_attn<float, DH, 8, 2>(a, grid, st);
+  else if (p.nw == 8) launch_attn<float, DH, 8, 1>(a, grid, st);
+  else if (p.nw == 4) launch_attn<float, DH, 4, 1>(a, grid, st);
+  else if (p.nw == 2) launch_attn<float, DH, 2, 1>(a, grid, st);
+  else launch_attn<float, DH, 1, 1>(a, grid, st);
+  if (p.nsplit > 1) launch_merge<float, DH>(a, st);
 }
 
 int attn_max_rows() { return 256; }
@@ -511,11 +786,11 @@ int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc,
     a.part_ml = a.part_o + size_t(p.nsplit) * rows * d.head_dim;
   }
   if (d.dtype == FDL_BF16) {
-    if (d.head_dim == 128) launch_attn_cfg<bf16_t, 128>(a, p, st);
-    else launch_attn_cfg<bf16_t, 64>(a, p, st);
+    if (d.head_dim == 128) launch_attn_bf16<128>(a, p, st);
+    else launch_attn_bf16<64>(a, p, st);
   } else {
-    if (d.head_dim == 128) launch_attn_cfg<float, 128>(a, p, st);
-    else launch_attn_cfg<float, 64>(a, p, st);
+    if (d.head_dim == 128) launch_attn_f32<128>(a, p, st);
+    else launch_attn_f32<64>(a, p, st);
   }
   return check_launch();
 }

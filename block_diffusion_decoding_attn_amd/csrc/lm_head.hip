@@ -237,8 +237,6 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
 // of 64 through LDS with the next slab prefetched into registers.
 constexpr int TB_V = 128, TB_M = 128, TB_K = 64, TB_PAD = 8, TB_ST = TB_K + TB_PAD;
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 __global__ __launch_bounds__(256) void lm_head_tiled_bf16(LmArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t As[TB_V * TB_ST];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[TB_M * TB_ST];
