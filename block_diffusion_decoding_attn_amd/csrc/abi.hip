@@ -9,6 +9,8 @@ int attn_max_rows();
 int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc, const void* vc,
                 const int32_t* prefix_len, const void* kb, const void* vb, void* out, float* lse, void* ws,
                 size_t ws_bytes, hipStream_t st);
+int prefill_launch(const fdl_dims& d, int q_start, int n_q, int n_keys, int causal, const void* q, const void* k,
+                   const void* v, void* out, float* lse, hipStream_t st);
 int lm_head_tiles(const fdl_dims& d);
 int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
                    hipStream_t st);
@@ -112,6 +114,19 @@ int fdl_block_attn(const fdl_dims* dims, int32_t block_idx, int32_t sub_idx, con
   if ((d.n_q_heads / d.n_kv_heads) * d.sub_block > attn_max_rows()) return FDL_E_UNSUPPORTED;
   return attn_launch(d, block_idx, q, k_cache, v_cache, prefix_len, k_blk, v_blk, out, lse, workspace,
                      workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int fdl_prefill_attn(const fdl_dims* dims, int32_t q_start, int32_t n_q, int32_t n_keys, int32_t causal,
+                     const void* q, const void* k, const void* v, void* out, float* lse, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  if (!q || !k || !v || !out) return FDL_E_INVAL;
+  if (n_q < 1 || q_start < 0 || n_keys < 1 || n_keys > d.prompt_len + d.gen_len) return FDL_E_INVAL;
+  if (causal != 0 && causal != 1) return FDL_E_INVAL;
+  if (d.dtype != FDL_BF16) return FDL_E_UNSUPPORTED;
+  if ((long long)q_start + n_q > (1 << 24) || d.n_q_heads > 65535) return FDL_E_UNSUPPORTED;
+  return prefill_launch(d, q_start, n_q, n_keys, causal, q, k, v, out, lse, reinterpret_cast<hipStream_t>(stream));
 }
 
 int fdl_lm_head(const fdl_dims* dims, int32_t rows, const void* x, const void* w, float* logits, void* stream) {

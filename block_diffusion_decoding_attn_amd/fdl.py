@@ -24,6 +24,7 @@ FDL_SELECT_THRESHOLD, FDL_SELECT_TOPK, FDL_SELECT_FACTOR = 0, 1, 2
 
 EXPORTS = (
     "fdl_version", "fdl_strerror", "fdl_dims_check", "fdl_block_attn_workspace_size", "fdl_block_attn",
+    "fdl_prefill_attn",
     "fdl_lm_head", "fdl_conf_select_workspace_size", "fdl_conf_select", "fdl_lm_head_select_workspace_size",
     "fdl_lm_head_select", "fdl_kv_append",
 )
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
             L.fdl_block_attn_workspace_size.restype = ctypes.c_size_t
             L.fdl_block_attn_workspace_size.argtypes = [_D]
             L.fdl_block_attn.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+            L.fdl_prefill_attn.argtypes = [_D, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
             L.fdl_lm_head.argtypes = [_D, _I, _P, _P, _P, _P]
             L.fdl_conf_select_workspace_size.restype = ctypes.c_size_t
             L.fdl_conf_select_workspace_size.argtypes = [_D, _I]
@@ -160,6 +162,24 @@ def fdl_block_attn(dims: fdl_dims, block_idx: int, sub_idx: int, q, k_cache, v_c
                               _ptr(prefix_len), _ptr(k_blk), _ptr(v_blk), _ptr(out), _ptr(lse), _ptr(workspace),
                               ws_bytes, _stream(stream))
     _check("fdl_block_attn", rc)
+    return out
+
+
+def fdl_prefill_attn(dims: fdl_dims, q_start: int, n_keys: int, causal: bool, q, k, v, out, lse=None,
+                     stream=None):
+    d = dims
+    dt = _dtype(d)
+    cap = d.prompt_len + d.gen_len
+    n_q = q.shape[1]
+    _expect("q", q, (d.batch, n_q, d.n_q_heads, d.head_dim), dt)
+    _expect("k", k, (d.batch, d.n_kv_heads, cap, d.head_dim), dt)
+    _expect("v", v, (d.batch, d.n_kv_heads, cap, d.head_dim), dt)
+    _expect("out", out, (d.batch, n_q, d.n_q_heads, d.head_dim), dt)
+    if lse is not None:
+        _expect("lse", lse, (d.batch, d.n_q_heads, n_q), torch.float32)
+    rc = lib().fdl_prefill_attn(ctypes.byref(d), q_start, n_q, n_keys, 1 if causal else 0, _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(out), _ptr(lse), _stream(stream))
+    _check("fdl_prefill_attn", rc)
     return out
 
 

@@ -146,6 +146,22 @@ int fdl_block_attn(const fdl_dims* dims, int32_t block_idx, int32_t sub_idx,
                    void* out, float* lse, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Multi-block attention: query positions q_start .. q_start + n_q - 1 of
+ * one sequence over its key positions 0 .. n_keys - 1 (eq 3).
+ *   causal = 1: block-causal, the M_BC pattern of "Fast-dLLM v2" (Attention
+ *     Mask Design): position p sees the keys of its own block and of every
+ *     earlier block (blocks of `block` positions), as in the prompt prefill.
+ *   causal = 0: every key visible, as in the Fast-dLLM v1 refresh of the
+ *     cached regions (Algorithm 1) and the PrefixCache recomputation.
+ *   q       [B][n_q][Hq][d] (bf16 only)
+ *   k, v    [B][Hkv][P+L][d]: positions 0 .. n_keys - 1 are read
+ *   out     [B][n_q][Hq][d], written
+ *   lse     [B][Hq][n_q] f32 natural-log log-sum-exp, or NULL
+ * Constraints: dtype FDL_BF16; n_q >= 1; q_start >= 0; 1 <= n_keys <= P + L. */
+int fdl_prefill_attn(const fdl_dims* dims, int32_t q_start, int32_t n_q, int32_t n_keys,
+                     int32_t causal, const void* q, const void* k, const void* v, void* out,
+                     float* lse, void* stream);
+
 /* LM head: logits[r][v] = sum_k X[r][k] * W[v][k], f32 accumulation and
  * output ("Fast-dLLM v2", Inference Pipeline Level 2: a distribution over the
  * vocabulary per position; with the token shift of Step 5 the row for block

@@ -160,6 +160,39 @@ def dense_masked_attention(q, k, v, mask):
     return out
 
 
+def bc_visible(p: int, j: int, block: int) -> bool:
+    """M_BC ([v2] "Attention Mask Design"): key j is visible to position p when
+    j's block is the same as or earlier than p's block."""
+    return block_of(j, block) <= block_of(p, block)
+
+
+def prefill_attention(q, k, v, q_start: int, n_keys: int, block: int, causal: bool = True):
+    """Attention of query positions q_start .. q_start+n_q-1 over key positions
+    0 .. n_keys-1 of one K/V sequence.
+
+    q [B][n_q][Hq][d]; k, v [B][Hkv][>= n_keys][d].  causal: the block-causal
+    M_BC pattern ([v2] "Attention Mask Design": a position sees its own block
+    and every earlier block), as in the prompt prefill; otherwise every key is
+    visible, as in the [v1] Algorithm 1 refresh.  Returns (out [B][n_q][Hq][d],
+    lse [B][Hq][n_q])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, nq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((B, nq, Hq, d))
+    lse = np.zeros((B, Hq, nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            for i in range(nq):
+                p = q_start + i
+                keys = [j for j in range(n_keys) if (bc_visible(p, j, block) or not causal)]
+                sc = k[b, g, keys] @ q[b, i, h] * score_scale(d)
+                w, l = softmax_weights(sc)
+                out[b, i, h] = w @ v[b, g, keys]
+                lse[b, h, i] = l
+    return out, lse
+
+
 # ----------------------------------------------------------------------------
 # LM head  ([v2] Inference Pipeline Level 2: distributions over the vocabulary)
 # ----------------------------------------------------------------------------

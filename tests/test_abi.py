@@ -89,6 +89,13 @@ def test_entry_points_reject_before_launch(L):
     # too many rows per KV head for one workgroup
     dbig = _dims(n_q_heads=28 * 2, n_kv_heads=2, sub_block=32)
     assert L.fdl_block_attn(by(dbig), 0, 0, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -2
+    # prefill / refresh attention
+    assert L.fdl_prefill_attn(by(d), 0, 0, 32, 1, fake, fake, fake, fake, None, None) == -1
+    assert L.fdl_prefill_attn(by(d), -1, 32, 32, 1, fake, fake, fake, fake, None, None) == -1
+    assert L.fdl_prefill_attn(by(d), 0, 32, 1537, 1, fake, fake, fake, fake, None, None) == -1
+    assert L.fdl_prefill_attn(by(d), 0, 32, 32, 2, fake, fake, fake, fake, None, None) == -1
+    assert L.fdl_prefill_attn(by(d), 0, 32, 32, 1, None, fake, fake, fake, None, None) == -1
+    assert L.fdl_prefill_attn(by(_dims("tiny_fp32")), 0, 32, 32, 1, fake, fake, fake, fake, None, None) == -2
     # lm head
     assert L.fdl_lm_head(by(d), 0, fake, fake, fake, None) == -1
     assert L.fdl_lm_head(by(d), 4, None, fake, fake, None) == -1

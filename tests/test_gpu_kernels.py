@@ -281,3 +281,25 @@ def test_lm_head_select_parity(B, R, H, V, dtype, mode):
     ref = O.conf_select(ref_logits.reshape(B, R, V), masked.numpy(), tau.numpy(), mode, 3, 1.5)
     st = compare_select(ref, got, masked.numpy(), tau.numpy(), mode, 3, 1.5, eps=1e-3)
     assert st["seq_checked"] + st["seq_excluded"] == B
+
+
+@pytest.mark.parametrize("kw,q_start,n_q,n_keys,causal", [
+    (dict(), 0, 196, 196, True),                    # prompt prefill of a whole ragged sequence
+    (dict(), 64, 70, 160, True),                    # a window of positions, keys past the window
+    (dict(n_q_heads=4, n_kv_heads=4), 0, 196, 196, False),   # v1 refresh: all keys visible
+    (dict(head_dim=64, block=16, sub_block=16), 5, 40, 100, True),
+    (dict(n_q_heads=28, n_kv_heads=4), 100, 33, 140, True),
+])
+def test_prefill_attn_parity(kw, q_start, n_q, n_keys, causal):
+    dev = _dev()
+    cfg = _cfg(**kw)
+    d = fdl.make_dims(cfg)
+    q = synth.normal((cfg.batch, n_q, cfg.n_q_heads, cfg.head_dim), 0, cfg.cfg_id, 30, n_q, dtype=cfg.torch_dtype)
+    k, v = synth.kv_cache(cfg)
+    out = torch.empty_like(q, device=dev)
+    lse = torch.empty((cfg.batch, cfg.n_q_heads, n_q), dtype=torch.float32, device=dev)
+    fdl.fdl_prefill_attn(d, q_start, n_keys, causal, q.to(dev), k.to(dev), v.to(dev), out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.prefill_attention(q, k, v, q_start, n_keys, cfg.block, causal)
+    assert normwise(out.float().cpu().numpy(), ref_o) <= 2e-2
+    assert np.abs(lse.cpu().numpy() - ref_l).max() <= 1e-3 * np.abs(ref_l).max()

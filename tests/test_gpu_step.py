@@ -141,3 +141,28 @@ def test_workload_step_parity(name, steps, seqs, groups, select, fused):
     print(name, select, "fused" if fused else "unfused", total)
     assert total["seq_checked"] >= 1
     assert total["token_checked"] >= 1
+
+
+@pytest.mark.parametrize("name,causal", [("llada-8b_dualcache", False), ("qwen2.5-7b_bs4", True)])
+def test_prefill_full_size_sampled(name, causal):
+    """Full-size multi-block attention: the v1 refresh over all P + L positions
+    (bidirectional) and the 7B prompt prefill (block-causal); the oracle
+    evaluates sampled heads and position windows in full."""
+    _need_gpu()
+    from block_diffusion_decoding_attn_amd import fdl
+    cfg = synth.get_config(name)
+    d = fdl.make_dims(cfg)
+    dev = torch.device("cuda")
+    n = cfg.cap if not causal else cfg.prompt_len
+    k, v = synth.kv_cache(cfg)
+    q = synth.normal((cfg.batch, n, cfg.n_q_heads, cfg.head_dim), 0, cfg.cfg_id, 31, dtype=cfg.torch_dtype)
+    out = torch.empty_like(q, device=dev)
+    fdl.fdl_prefill_attn(d, 0, n, causal, q.to(dev), k.to(dev), v.to(dev), out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    for b, h, p0 in [(0, 0, 0), (cfg.batch - 1, cfg.n_q_heads - 1, n - 16), (0, cfg.n_q_heads // 2, n // 2 + 3)]:
+        g = h // G
+        ref, _ = O.prefill_attention(q[b:b + 1, p0:p0 + 16, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                                     p0, n, cfg.block, causal)
+        assert normwise(got[b:b + 1, p0:p0 + 16, h:h + 1], ref) <= 2e-2, (b, h, p0)

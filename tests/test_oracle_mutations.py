@@ -126,7 +126,17 @@ def _m_no_fallback(conf, masked, tau, mode=O.SELECT_THRESHOLD, k=0, factor=1.0):
     return np.asarray(masked, bool) & (np.asarray(conf) > tau)
 
 
+def _m_bc_strict(p, j, block):
+    return O.block_of(j, block) < O.block_of(p, block)
+
+
+def _m_bc_token_causal(p, j, block):
+    return j <= p
+
+
 MUTATIONS = [
+    ("prefill: strictly earlier blocks only", "bc_visible", _m_bc_strict),
+    ("prefill: token-causal instead of block-causal", "bc_visible", _m_bc_token_causal),
     ("score scale 1/d instead of 1/sqrt(d)", "score_scale", _m_scale),
     ("GQA head h % Hkv instead of h // G", "kv_head_of", _m_gqa),
     (">= tau instead of > tau", "above_threshold", _m_ge),

@@ -412,3 +412,42 @@ def test_c8_append_reproduces_concatenation():
         assert not cache[b, :, cat.shape[1]:].any()
     with pytest.raises(ValueError):
         O.kv_append(cache, r.standard_normal((B, Hkv, 8, d)), ln)
+
+
+# ----------------------------------------------------------------------------
+# prefill / refresh attention (multi-block queries)
+# ----------------------------------------------------------------------------
+
+def test_prefill_rows_equal_cached_block_steps():
+    """Block-causal prefill of a sequence: the rows of each block equal the
+    cached step of that block (prefix = everything before it, block = itself)."""
+    r = rng(20)
+    B, Hq, Hkv, d, D, T = 2, 4, 2, 8, 8, 40
+    q = r.standard_normal((B, T, Hq, d))
+    k, v = r.standard_normal((B, Hkv, T, d)), r.standard_normal((B, Hkv, T, d))
+    out, lse = O.prefill_attention(q, k, v, 0, T, D, causal=True)
+    for blk in range(T // D):
+        lp = blk * D
+        o2, l2 = O.block_attention(q[:, lp:lp + D], k, v, k[:, :, lp:lp + D], v[:, :, lp:lp + D], [lp] * B)
+        np.testing.assert_allclose(out[:, lp:lp + D], o2, atol=1e-12)
+        np.testing.assert_allclose(lse[:, :, lp:lp + D], l2, atol=1e-12)
+
+
+def test_prefill_key_counts_and_bidirectional():
+    """q = 0 gives equal scores, so lse = ln(number of visible keys): the
+    block end for the causal rule (capped at n_keys), all n_keys otherwise;
+    the bidirectional form equals the DualCache step with the block fresh."""
+    r = rng(21)
+    B, Hq, Hkv, d, D, nk = 1, 2, 1, 4, 8, 30
+    q0 = np.zeros((B, 12, Hq, d))
+    k, v = r.standard_normal((B, Hkv, 32, d)), r.standard_normal((B, Hkv, 32, d))
+    _, lse = O.prefill_attention(q0, k, v, 10, nk, D, causal=True)
+    for i in range(12):
+        p = 10 + i
+        assert abs(lse[0, 0, i] - math.log(min(nk, (p // D + 1) * D))) < 1e-14
+    _, lse = O.prefill_attention(q0, k, v, 10, nk, D, causal=False)
+    np.testing.assert_allclose(lse, math.log(nk), atol=1e-14)
+    q = r.standard_normal((B, D, Hq, d))
+    out, _ = O.prefill_attention(q, k, v, 16, 32, D, causal=False)
+    o2, _ = O.block_attention(q, k, v, k[:, :, 16:24], v[:, :, 16:24], [16], mode=O.DUAL_CACHE, total_len=32)
+    np.testing.assert_allclose(out, o2, atol=1e-12)
