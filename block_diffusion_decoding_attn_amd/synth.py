@@ -279,3 +279,59 @@ def schedule(cfg: Config) -> List[Tuple[int, int, bool]]:
         for s in range(cfg.subs_per_block):
             out.append((b, s, s == cfg.subs_per_block - 1))
     return out
+
+
+# ----------------------------------------------------------------------------
+# Decode-loop inputs
+# ----------------------------------------------------------------------------
+
+T_PROMPT, T_EOS = 15, 16
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """Inputs of one run of the decode loop (whole generation of a batch).
+
+    prompt [B][P] int32 token ids; boost_tok/boost_val [B][L] the drawn token
+    and boost of every generated position (int32 / float32); tau [B] float32;
+    eos_at [B] the generated position whose boost targets EOS (>= L: none);
+    mask_id / eos_id the two reserved token ids; gain the attention-output
+    gain of the stand-in model."""
+    prompt: torch.Tensor
+    boost_tok: torch.Tensor
+    boost_val: torch.Tensor
+    tau: torch.Tensor
+    eos_at: torch.Tensor
+    mask_id: int
+    eos_id: int
+    gain: float
+
+
+def reserved_ids(vocab: int) -> Tuple[int, int]:
+    """(mask_id, eos_id): the last two ids of the vocabulary."""
+    return vocab - 1, vocab - 2
+
+
+def decode_inputs(cfg: Config, seed: int = 0, boost: str = "calibrated", gain: float = 2.0,
+                  eos: bool = True) -> DecodeInputs:
+    """Seeded inputs of the decode loop.
+
+    Prompt tokens and the boost targets are uniform over the ordinary ids
+    0..V-3; boosts are U(0,12) (+ shift, as for the single-step rows).  With
+    eos, each sequence draws eos_at ~ U{0..2L-1}: when it falls inside the
+    generation, that position's boost targets EOS with the top boost
+    12 (+ shift), so about half of the sequences stop early, at different
+    blocks (the padded-batch case)."""
+    B, P, L, V = cfg.batch, cfg.prompt_len, cfg.gen_len, cfg.vocab
+    mask_id, eos_id = reserved_ids(V)
+    prompt = randint((B, P), seed, cfg.cfg_id, T_PROMPT, 0, 0, V - 2).to(torch.int32)
+    tok = randint((B, L), seed, cfg.cfg_id, T_BOOST_TOK, 7777, 0, V - 2)
+    val = uniform((B, L), seed, cfg.cfg_id, T_BOOST_VAL, 7777, 0.0, 12.0) + boost_shift(V, boost)
+    eos_at = randint((B,), seed, cfg.cfg_id, T_EOS, 0, 0, 2 * L) if eos else torch.full((B,), 2 * L)
+    for b in range(B):
+        p = int(eos_at[b])
+        if p < L:
+            tok[b, p] = eos_id
+            val[b, p] = 12.0 + boost_shift(V, boost)
+    return DecodeInputs(prompt, tok.to(torch.int32), val.to(torch.float32), taus(cfg, 0, seed), eos_at,
+                        mask_id, eos_id, gain)

@@ -1,18 +1,20 @@
 """Each plausible mistake planted in the oracle (on the CPU, via monkeypatch)
-must make at least one pin in test_oracle_pins fail."""
-import inspect
+must make at least one pin fail: those of test_oracle_pins for the step
+functions, those of test_decode_oracle_pins for the decode loop."""
 import math
 
 import numpy as np
 import pytest
 
+import test_decode_oracle_pins as DP
 import test_oracle_pins as P
+from oracle import fdl_decode_oracle as D
 from oracle import fdl_oracle as O
 
 
-def _pins():
+def _pins(module):
     out = []
-    for name, fn in sorted(vars(P).items()):
+    for name, fn in sorted(vars(module).items()):
         if not name.startswith("test_") or not callable(fn):
             continue
         marks = getattr(fn, "pytestmark", [])
@@ -25,9 +27,9 @@ def _pins():
     return out
 
 
-def _failures():
+def _failures(module=P):
     bad = []
-    for name, fn, args in _pins():
+    for name, fn, args in _pins(module):
         try:
             fn(*args)
         except Exception:          # noqa: BLE001 - any failure counts
@@ -36,7 +38,8 @@ def _failures():
 
 
 def test_pins_all_pass_unmutated():
-    assert _failures() == []
+    assert _failures(P) == []
+    assert _failures(DP) == []
 
 
 def _m_scale(d):
@@ -134,6 +137,48 @@ def _m_bc_token_causal(p, j, block):
     return j <= p
 
 
+_orig_embed_kv = D.embed_kv
+
+
+def _m_embed_kv_prev_token(w64, tokens_row, positions, hq, hkv, d):
+    return _orig_embed_kv(w64, tokens_row, [max(p - 1, 0) for p in positions], hq, hkv, d)
+
+
+def _m_sub_rows_no_block(block_size, sub_size, blk, sub):
+    return range(sub * sub_size, sub * sub_size + sub_size)
+
+
+def _m_never_eos(block_tokens, eos_id):
+    return False
+
+
+def _m_block_start_late(prompt_len, block_size, blk):
+    return prompt_len + blk * block_size + 1
+
+
+_orig_sm_embed = D.sm_embed
+
+
+def _m_value_not_reversed(w64, token, hq, hkv, d):
+    q, k, v = _orig_sm_embed(w64, token, hq, hkv, d)
+    return q, k, v[:, ::-1]
+
+
+def _m_hidden_no_attention(o_heads, w64, boost_tok, boost_val, gain):
+    wt = w64[boost_tok]
+    return boost_val * wt / float(wt @ wt) + 0.0 * o_heads.reshape(-1)
+
+
+DECODE_MUTATIONS = [
+    ("decode: K/V embedded from the previous position's token", "embed_kv", _m_embed_kv_prev_token),
+    ("decode: sub-block rows without the block offset", "sub_rows", _m_sub_rows_no_block),
+    ("decode: EOS never stops a sequence", "holds_eos", _m_never_eos),
+    ("decode: block starts one position late", "block_start", _m_block_start_late),
+    ("decode: value slice not reversed", "sm_embed", _m_value_not_reversed),
+    ("decode: hidden row without the attention output", "sm_hidden", _m_hidden_no_attention),
+]
+
+
 MUTATIONS = [
     ("prefill: strictly earlier blocks only", "bc_visible", _m_bc_strict),
     ("prefill: token-causal instead of block-causal", "bc_visible", _m_bc_token_causal),
@@ -158,5 +203,12 @@ MUTATIONS = [
 @pytest.mark.parametrize("label,attr,fn", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(monkeypatch, label, attr, fn):
     monkeypatch.setattr(O, attr, fn)
-    bad = _failures()
+    bad = _failures(P)
+    assert bad, f"no pin caught: {label}"
+
+
+@pytest.mark.parametrize("label,attr,fn", DECODE_MUTATIONS, ids=[m[0] for m in DECODE_MUTATIONS])
+def test_planted_decode_mistake_is_caught(monkeypatch, label, attr, fn):
+    monkeypatch.setattr(D, attr, fn)
+    bad = _failures(DP)
     assert bad, f"no pin caught: {label}"
