@@ -1,29 +1,11 @@
 // C ABI entry points of libfdl: host-side validation, then kernel launches.
 // Nothing here allocates device memory or synchronizes with the device.
 #include "common.h"
+#include "launch.h"
+
+#include <cmath>
 
 namespace fdl {
-
-size_t attn_workspace_bytes(const fdl_dims& d);
-int attn_max_rows();
-int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc, const void* vc,
-                const int32_t* prefix_len, const void* kb, const void* vb, void* out, float* lse, void* ws,
-                size_t ws_bytes, hipStream_t st);
-int prefill_launch(const fdl_dims& d, int q_start, int n_q, int n_keys, int causal, const void* q, const void* k,
-                   const void* v, void* out, float* lse, hipStream_t st);
-int lm_head_tiles(const fdl_dims& d);
-int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
-                   hipStream_t st);
-int select_finalize_launch(const fdl_dims& d, int R, const void* part, int nc, const uint8_t* masked,
-                           const float* tau, int mode, int k, float factor, int32_t* token_out, float* conf_out,
-                           uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
-                           hipStream_t st);
-size_t select_workspace_bytes(const fdl_dims& d, int rows_per_seq);
-int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* masked, const float* tau, int mode,
-                  int k, float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out, int32_t* n_commit,
-                  int32_t* tokens_inout, uint8_t* masked_inout, void* ws, size_t ws_bytes, hipStream_t st);
-int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int n_new, int32_t* len,
-                  hipStream_t st);
 
 int dtype_size(int dtype) { return dtype == FDL_F32 ? 4 : 2; }
 
@@ -72,6 +54,44 @@ static int check_lm_head_args(const fdl_dims& d, int32_t rows, const void* x, co
   if (d.dtype == FDL_BF16 && d.hidden % 64 != 0) return FDL_E_UNSUPPORTED;
   if (d.dtype == FDL_F32 && (d.hidden % 4 != 0 || rows > 64)) return FDL_E_UNSUPPORTED;
   if ((long long)rows * d.vocab > (1LL << 40)) return FDL_E_UNSUPPORTED;
+  return FDL_OK;
+}
+
+// Arguments of the decode loop beyond the dims.
+static int check_decode(const fdl_dims& d, const fdl_decode_args* g) {
+  if (!g) return FDL_E_INVAL;
+  if (!g->w || !g->boost_tok || !g->boost_val || !g->k_cache || !g->v_cache || !g->len || !g->tokens ||
+      !g->masked || !g->seq_steps || !g->eos_block || !g->counters)
+    return FDL_E_INVAL;
+  if (d.prompt_len > 0 && !g->prompt) return FDL_E_INVAL;
+  if (g->mask_id < 0 || g->mask_id >= d.vocab || g->eos_id < 0 || g->eos_id >= d.vocab) return FDL_E_INVAL;
+  if (!std::isfinite(g->gain)) return FDL_E_INVAL;
+  const int nb = d.gen_len / d.block;
+  if (g->max_blocks < 0 || g->max_blocks > nb) return FDL_E_INVAL;
+  const int S = d.sub_block;
+  if (S > 256) return FDL_E_INVAL;
+  if ((long long)d.batch * S > 65535) return FDL_E_UNSUPPORTED;  // select grid extent
+  if (g->mode == FDL_SELECT_THRESHOLD) {
+    if (!g->tau) return FDL_E_INVAL;
+  } else if (g->mode == FDL_SELECT_TOPK) {
+    if (g->k < 1) return FDL_E_INVAL;
+  } else if (g->mode == FDL_SELECT_FACTOR) {
+    if (!(g->factor > 0.f)) return FDL_E_INVAL;
+  } else {
+    return FDL_E_INVAL;
+  }
+  const int rc = check_lm_head_args(d, d.batch * S, g->w, g->w);
+  if (rc != FDL_OK) return rc;
+  if ((long long)d.n_q_heads * d.head_dim != d.hidden) return FDL_E_UNSUPPORTED;  // the stand-in model
+  if ((d.n_q_heads / d.n_kv_heads) * S > attn_max_rows()) return FDL_E_UNSUPPORTED;
+  const bool any = g->trace_meta || g->trace_tokens || g->trace_masked || g->trace_token || g->trace_conf;
+  const bool all = g->trace_meta && g->trace_tokens && g->trace_masked && g->trace_token && g->trace_conf;
+  if (any && !all) return FDL_E_INVAL;
+  if (all) {
+    const long long slots = (long long)(g->max_blocks > 0 ? g->max_blocks : nb) * (d.block / S) *
+                            decode_slots_per_sub(d, g->mode, g->k);
+    if (g->trace_cap < slots) return FDL_E_INVAL;
+  }
   return FDL_OK;
 }
 
@@ -194,6 +214,32 @@ int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void
   if (!k_cache || !v_cache || !k_new || !v_new || !len) return FDL_E_INVAL;
   if (n_new < 1 || n_new > d.prompt_len + d.gen_len) return FDL_E_INVAL;
   return append_launch(d, k_cache, v_cache, k_new, v_new, n_new, len, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t fdl_decode_workspace_size(const fdl_dims* dims) {
+  if (check_dims(dims) != FDL_OK) return 0;
+  return decode_workspace_bytes(*dims);
+}
+
+int32_t fdl_decode_step_slots(const fdl_dims* dims, int32_t mode, int32_t k, int32_t max_blocks) {
+  if (check_dims(dims) != FDL_OK) return 0;
+  const int nb = dims->gen_len / dims->block;
+  if (max_blocks < 0 || max_blocks > nb) return 0;
+  if (mode != FDL_SELECT_THRESHOLD && mode != FDL_SELECT_TOPK && mode != FDL_SELECT_FACTOR) return 0;
+  if (mode == FDL_SELECT_TOPK && k < 1) return 0;
+  return (max_blocks > 0 ? max_blocks : nb) * (dims->block / dims->sub_block) *
+         decode_slots_per_sub(*dims, mode, k);
+}
+
+int fdl_decode(const fdl_dims* dims, const fdl_decode_args* args, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  rc = check_decode(d, args);
+  if (rc != FDL_OK) return rc;
+  if (!workspace || workspace_bytes < decode_workspace_bytes(d)) return FDL_E_WORKSPACE;
+  return decode_launch(d, *args, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

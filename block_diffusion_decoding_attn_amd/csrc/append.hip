@@ -22,9 +22,11 @@ struct AppendArgs {
   int32_t* len;
   int B, Hkv, cap, n_new;
   int row_bytes;  // head_dim * element size
+  const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
 };
 
 __global__ __launch_bounds__(256) void kv_append_copy_kernel(AppendArgs a) {
+  if (gate_closed(a.gate)) return;
   const int b = blockIdx.z;
   const int kv = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
   const int lo = a.len[b];
@@ -37,7 +39,8 @@ __global__ __launch_bounds__(256) void kv_append_copy_kernel(AppendArgs a) {
     st16(dst + i * 16, ld16(src + i * 16));
 }
 
-__global__ void kv_append_len_kernel(int32_t* len, int B, int cap, int n_new) {
+__global__ void kv_append_len_kernel(int32_t* len, int B, int cap, int n_new, const int32_t* gate) {
+  if (gate_closed(gate)) return;
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int lo = len[b];
@@ -46,9 +49,9 @@ __global__ void kv_append_len_kernel(int32_t* len, int B, int cap, int n_new) {
 }
 
 int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int n_new, int32_t* len,
-                  hipStream_t st) {
+                  hipStream_t st, const int32_t* gate) {
   AppendArgs a;
-  a.kc = kc; a.vc = vc; a.kn = kn; a.vn = vn; a.len = len;
+  a.kc = kc; a.vc = vc; a.kn = kn; a.vn = vn; a.len = len; a.gate = gate;
   a.B = d.batch; a.Hkv = d.n_kv_heads; a.cap = d.prompt_len + d.gen_len; a.n_new = n_new;
   a.row_bytes = d.head_dim * dtype_size(d.dtype);
   const size_t n16 = size_t(n_new) * a.row_bytes / 16;
@@ -56,7 +59,7 @@ int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const v
   if (chunks > 64) chunks = 64;
   hipLaunchKernelGGL(kv_append_copy_kernel, dim3(chunks, 2 * d.n_kv_heads, d.batch), dim3(256), 0, st, a);
   hipLaunchKernelGGL(kv_append_len_kernel, dim3((d.batch + 255) / 256), dim3(256), 0, st, len, d.batch, a.cap,
-                     n_new);
+                     n_new, gate);
   return check_launch();
 }
 

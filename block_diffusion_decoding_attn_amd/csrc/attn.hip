@@ -45,6 +45,7 @@ struct AttnArgs {
   int nsplit;
   int split_keys;
   float scale_log2;
+  const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
 };
 
 template <typename T>
@@ -85,6 +86,7 @@ __device__ __forceinline__ void store4(float* p, f32x4 v, float s) {
 // f32 data (and the generic 16-row layout): 16x16x4 f32 MFMA.
 template <typename T, int DH, int NW, int RB>
 __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
+  if (gate_closed(a.gate)) return;
   typedef Frag<T> F;
   constexpr int NT = NW * 64;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
@@ -375,6 +377,7 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
 // normalization is unchanged, and the O/l rescale is skipped on most tiles.
 template <int DH, int NW>
 __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
+  if (gate_closed(a.gate)) return;
   constexpr int RB = 1;
   constexpr int KSTEPS = DH / 16, DT = DH / 32;
   typedef bf16_t T;
@@ -630,6 +633,7 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
 // were written by workgroups on other XCDs and come back from beyond L2).
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void block_attn_merge_kernel(AttnArgs a) {
+  if (gate_closed(a.gate)) return;
   constexpr int TPR = DH / 4;  // threads per row, 4 dims each
   constexpr int U = 8;
   const int n_rows = a.B * a.Hq * a.S;
@@ -760,7 +764,7 @@ int attn_max_rows() { return 256; }
 
 int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc, const void* vc,
                 const int32_t* prefix_len, const void* kb, const void* vb, void* out, float* lse,
-                void* ws, size_t ws_bytes, hipStream_t st) {
+                void* ws, size_t ws_bytes, hipStream_t st, const int32_t* gate) {
   const int cap = d.prompt_len + d.gen_len;
   const int default_lp = d.prompt_len + block_idx * d.block;
   // grid covers the longest key list any sequence can have at this step
@@ -778,6 +782,7 @@ int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc,
   a.split_keys = p.split_keys;
   a.scale_log2 = kLog2e / sqrtf(float(d.head_dim));
   a.part_o = nullptr; a.part_ml = nullptr;
+  a.gate = gate;
   if (p.nsplit > 1) {
     const size_t rows = size_t(d.batch) * d.n_q_heads * d.sub_block;
     const size_t need = size_t(p.nsplit) * rows * (d.head_dim + 2) * sizeof(float);

@@ -99,6 +99,10 @@ __device__ __forceinline__ void push(Red& r, float x, int v) {
   }
 }
 
+// Device-side gate of the decode loop: a launch whose gate word reads 0 does no
+// work (every thread returns before its first barrier).  A null gate: always run.
+__device__ __forceinline__ bool gate_closed(const int32_t* gate) { return gate != nullptr && *gate == 0; }
+
 __device__ __forceinline__ f32x4 pack_red(Red r) { return f32x4{r.m, r.s, __int_as_float(r.i), 0.f}; }
 __device__ __forceinline__ Red unpack_red(f32x4 p) { return Red{p[0], p[1], __float_as_int(p[2])}; }
 __device__ __forceinline__ Red red_empty() { return Red{-INFINITY, 0.f, 0x7fffffff}; }

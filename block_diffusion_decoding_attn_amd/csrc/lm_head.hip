@@ -22,6 +22,7 @@ struct LmArgs {
   float* out;    // [M][V] logits, or null (fused select: only partials)
   f32x4* part;   // [M][nc] confidence partials per 128-row vocabulary tile, or null
   int M, H, V, nc;
+  const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
 };
 
 // Fused-select epilogue, shared by the skinny kernels: lane holds
@@ -68,6 +69,7 @@ __device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (
 // 4.5 TB/s when every wave fetched its own X fragments).
 template <int NTM, int ROWS, int KSLAB, int WPB>
 __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
+  if (gate_closed(a.gate)) return;
   constexpr int NT = WPB * 64;
   constexpr int CPR = KSLAB * 2 / 16;        // 16-byte chunks per row of a slab
   constexpr int WCH = ROWS * CPR;            // W chunks per slab
@@ -185,6 +187,7 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
 // 16x16x4 f32 MFMA, one k value per lane per instruction.
 template <int NTM, int RT>
 __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
+  if (gate_closed(a.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int v0 = (blockIdx.x * 4 + wave) * RT * 16;
@@ -238,6 +241,7 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
 constexpr int TB_V = 128, TB_M = 128, TB_K = 64, TB_PAD = 8, TB_ST = TB_K + TB_PAD;
 
 __global__ __launch_bounds__(256) void lm_head_tiled_bf16(LmArgs a) {
+  if (gate_closed(a.gate)) return;
   __shared__ __attribute__((aligned(16))) bf16_t As[TB_V * TB_ST];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[TB_M * TB_ST];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -382,8 +386,8 @@ static void launch_skinny_f32(const LmArgs& a, hipStream_t st) {
 int lm_head_tiles(const fdl_dims& d) { return (d.vocab + 127) / 128; }
 
 int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
-                   hipStream_t st) {
-  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d)};
+                   hipStream_t st, const int32_t* gate) {
+  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d), gate};
   const int ntm = (rows + 15) / 16;
   if (d.dtype == FDL_BF16) {
     switch (ntm) {

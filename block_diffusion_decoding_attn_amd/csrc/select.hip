@@ -35,11 +35,14 @@ struct SelArgs {
   uint8_t* masked_inout;
   f32x4* part;  // [M][NC] (max, sum, argmax bits, 0)
   int B, R, V, NC, chunk;
+  int sstride;          // elements between sequences in masked / tokens_inout / masked_inout
+  const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
 };
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void select_partial_kernel(SelArgs a) {
   __shared__ Red sh[4];
+  if (gate_closed(a.gate)) return;
   const int row = blockIdx.y, c = blockIdx.x;
   const int v_begin = c * a.chunk;
   const int v_end = min(v_begin + a.chunk, a.V);
@@ -84,6 +87,7 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   __shared__ int tok_s[256];
   __shared__ int cand_s[256];
   __shared__ int red_i[256];
+  if (gate_closed(a.gate)) return;
   const int b = blockIdx.x, tid = threadIdx.x;
   int rpow = 1;
   while (rpow < a.R) rpow <<= 1;
@@ -115,12 +119,13 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   const int r = tid;
   const bool live = r < a.R;
   const size_t row = size_t(b) * a.R + r;
+  const size_t srow = size_t(b) * a.sstride + r;  // row in the per-sequence state arrays
   float conf = 0.f;
   int tok = 0, cand = 0;
   if (live) {
     conf = conf_s[r];
     tok = tok_s[r];
-    cand = a.masked[row] != 0;
+    cand = a.masked[srow] != 0;
     a.token_out[row] = tok;
     a.conf_out[row] = conf;
   }
@@ -177,8 +182,8 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   if (r == 0) a.n_commit[b] = n_sel;
   if (live) {
     a.commit_out[row] = sel ? 1 : 0;
-    if (sel && a.tokens_inout) a.tokens_inout[row] = tok;
-    if (sel && a.masked_inout) a.masked_inout[row] = 0;
+    if (sel && a.tokens_inout) a.tokens_inout[srow] = tok;
+    if (sel && a.masked_inout) a.masked_inout[srow] = 0;
   }
 }
 
@@ -205,7 +210,7 @@ size_t select_workspace_bytes(const fdl_dims& d, int rows_per_seq) {
 int select_finalize_launch(const fdl_dims& d, int R, const void* part, int nc, const uint8_t* masked,
                            const float* tau, int mode, int k, float factor, int32_t* token_out, float* conf_out,
                            uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
-                           hipStream_t st) {
+                           hipStream_t st, int state_stride, const int32_t* gate) {
   SelArgs a;
   a.logits = nullptr; a.masked = masked; a.tau = tau;
   a.mode = mode; a.k = k; a.factor = factor;
@@ -213,6 +218,8 @@ int select_finalize_launch(const fdl_dims& d, int R, const void* part, int nc, c
   a.tokens_inout = tokens_inout; a.masked_inout = masked_inout;
   a.B = d.batch; a.R = R; a.V = d.vocab;
   a.NC = nc; a.chunk = 0;
+  a.sstride = state_stride > 0 ? state_stride : R;
+  a.gate = gate;
   a.part = reinterpret_cast<f32x4*>(const_cast<void*>(part));
   hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch), dim3(FIN_NT), 0, st, a);
   return check_launch();
@@ -227,6 +234,8 @@ int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* 
   a.token_out = token_out; a.conf_out = conf_out; a.commit_out = commit_out; a.n_commit = n_commit;
   a.tokens_inout = tokens_inout; a.masked_inout = masked_inout;
   a.B = d.batch; a.R = R; a.V = d.vocab;
+  a.sstride = R;
+  a.gate = nullptr;
   select_plan(d.batch * R, d.vocab, a.NC, a.chunk);
   const size_t need = size_t(d.batch) * R * a.NC * sizeof(f32x4);
   if (!ws || ws_bytes < need) return FDL_E_WORKSPACE;

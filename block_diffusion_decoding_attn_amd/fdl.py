@@ -26,7 +26,7 @@ EXPORTS = (
     "fdl_version", "fdl_strerror", "fdl_dims_check", "fdl_block_attn_workspace_size", "fdl_block_attn",
     "fdl_prefill_attn",
     "fdl_lm_head", "fdl_conf_select_workspace_size", "fdl_conf_select", "fdl_lm_head_select_workspace_size",
-    "fdl_lm_head_select", "fdl_kv_append",
+    "fdl_lm_head_select", "fdl_kv_append", "fdl_decode_workspace_size", "fdl_decode_step_slots", "fdl_decode",
 )
 
 
@@ -40,6 +40,20 @@ class fdl_dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "prompt_len", "gen_len", "block", "sub_block", "n_q_heads", "n_kv_heads", "head_dim",
         "hidden", "vocab", "dtype", "attn_mode")]
+
+
+class fdl_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.c_void_p), ("gain", ctypes.c_float), ("mask_id", ctypes.c_int32), ("eos_id", ctypes.c_int32),
+        ("prompt", ctypes.c_void_p), ("boost_tok", ctypes.c_void_p), ("boost_val", ctypes.c_void_p),
+        ("tau", ctypes.c_void_p), ("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("factor", ctypes.c_float),
+        ("max_blocks", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("len", ctypes.c_void_p),
+        ("tokens", ctypes.c_void_p), ("masked", ctypes.c_void_p), ("seq_steps", ctypes.c_void_p),
+        ("eos_block", ctypes.c_void_p), ("counters", ctypes.c_void_p),
+        ("trace_cap", ctypes.c_int32), ("trace_meta", ctypes.c_void_p), ("trace_tokens", ctypes.c_void_p),
+        ("trace_masked", ctypes.c_void_p), ("trace_token", ctypes.c_void_p), ("trace_conf", ctypes.c_void_p),
+    ]
 
 
 def make_dims(cfg, batch: Optional[int] = None) -> fdl_dims:
@@ -88,6 +102,11 @@ def lib() -> ctypes.CDLL:
             L.fdl_lm_head_select.argtypes = [_D, _I, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_size_t, _P]
             L.fdl_kv_append.argtypes = [_D, _P, _P, _P, _P, _I, _P, _P]
+            L.fdl_decode_workspace_size.restype = ctypes.c_size_t
+            L.fdl_decode_workspace_size.argtypes = [_D]
+            L.fdl_decode_step_slots.restype = ctypes.c_int32
+            L.fdl_decode_step_slots.argtypes = [_D, _I, _I, _I]
+            L.fdl_decode.argtypes = [_D, ctypes.POINTER(fdl_decode_args), _P, ctypes.c_size_t, _P]
             _lib = L
     return _lib
 
@@ -268,3 +287,55 @@ def fdl_kv_append(dims: fdl_dims, k_cache, v_cache, k_new, v_new, length, stream
     rc = lib().fdl_kv_append(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), n_new,
                              _ptr(length), _stream(stream))
     _check("fdl_kv_append", rc)
+
+
+def fdl_decode_workspace_size(dims: fdl_dims) -> int:
+    return lib().fdl_decode_workspace_size(ctypes.byref(dims))
+
+
+def fdl_decode_step_slots(dims: fdl_dims, mode: int, k: int, max_blocks: int) -> int:
+    return lib().fdl_decode_step_slots(ctypes.byref(dims), mode, k, max_blocks)
+
+
+def fdl_decode(dims: fdl_dims, w, prompt, boost_tok, boost_val, tau, mode: int, k: int, factor: float,
+               mask_id: int, eos_id: int, gain: float, max_blocks: int, k_cache, v_cache, length, tokens, masked,
+               seq_steps, eos_block, counters, trace=None, workspace=None, stream=None):
+    """trace: None, or a dict of tensors meta [T][2], tokens [T][B][D], masked
+    [T][B][D], token [T][B][S], conf [T][B][S]."""
+    d = dims
+    dt = _dtype(d)
+    B, P, L, D, S = d.batch, d.prompt_len, d.gen_len, d.block, d.sub_block
+    cap = P + L
+    _expect("w", w, (d.vocab, d.hidden), dt)
+    if P > 0:
+        _expect("prompt", prompt, (B, P), torch.int32)
+    _expect("boost_tok", boost_tok, (B, L), torch.int32)
+    _expect("boost_val", boost_val, (B, L), torch.float32)
+    if tau is not None:
+        _expect("tau", tau, (B,), torch.float32)
+    _expect("k_cache", k_cache, (B, d.n_kv_heads, cap, d.head_dim), dt)
+    _expect("v_cache", v_cache, (B, d.n_kv_heads, cap, d.head_dim), dt)
+    _expect("len", length, (B,), torch.int32)
+    _expect("tokens", tokens, (B, cap), torch.int32)
+    _expect("masked", masked, (B, cap), torch.uint8)
+    _expect("seq_steps", seq_steps, (B,), torch.int32)
+    _expect("eos_block", eos_block, (B,), torch.int32)
+    _expect("counters", counters, (2,), torch.int32)
+    a = fdl_decode_args(w=_ptr(w), gain=gain, mask_id=mask_id, eos_id=eos_id, prompt=_ptr(prompt) if P else None,
+                        boost_tok=_ptr(boost_tok), boost_val=_ptr(boost_val), tau=_ptr(tau), mode=mode, k=k,
+                        factor=factor, max_blocks=max_blocks, k_cache=_ptr(k_cache), v_cache=_ptr(v_cache),
+                        len=_ptr(length), tokens=_ptr(tokens), masked=_ptr(masked), seq_steps=_ptr(seq_steps),
+                        eos_block=_ptr(eos_block), counters=_ptr(counters), trace_cap=0)
+    if trace is not None:
+        T = trace["meta"].shape[0]
+        _expect("trace meta", trace["meta"], (T, 2), torch.int32)
+        _expect("trace tokens", trace["tokens"], (T, B, D), torch.int32)
+        _expect("trace masked", trace["masked"], (T, B, D), torch.uint8)
+        _expect("trace token", trace["token"], (T, B, S), torch.int32)
+        _expect("trace conf", trace["conf"], (T, B, S), torch.float32)
+        a.trace_cap = T
+        a.trace_meta, a.trace_tokens, a.trace_masked = (_ptr(trace[n]) for n in ("meta", "tokens", "masked"))
+        a.trace_token, a.trace_conf = _ptr(trace["token"]), _ptr(trace["conf"])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().fdl_decode(ctypes.byref(d), ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("fdl_decode", rc)

@@ -158,3 +158,71 @@ class StepRunner:
             self.select(i)
         if inp.append_after and not self.dual:
             self.append(i)
+
+
+class DecodeRunner:
+    """Device buffers of one run of the decode loop (fdl_decode): a whole
+    generation of the batch from the prompt, with the stand-in model of the
+    library (tied embedding w, attention-output gain, per-position boost)."""
+
+    def __init__(self, cfg: synth.Config, seed: int = 0, boost: str = "calibrated", gain: float = 2.0,
+                 select: str = "threshold", k: int = 4, factor: float = 1.0, max_blocks: int = 0,
+                 trace: bool = True, eos: bool = True, inputs: Optional[synth.DecodeInputs] = None,
+                 device: str = "cuda", w_host: Optional[torch.Tensor] = None):
+        self.cfg, self.seed = cfg, seed
+        self.mode = {"threshold": fdl.FDL_SELECT_THRESHOLD, "topk": fdl.FDL_SELECT_TOPK,
+                     "factor": fdl.FDL_SELECT_FACTOR}[select]
+        self.select, self.k, self.factor, self.max_blocks = select, k, factor, max_blocks
+        self.inp = synth.decode_inputs(cfg, seed, boost, gain, eos) if inputs is None else inputs
+        self.dims = fdl.make_dims(cfg)
+        dev = self.dev = torch.device(device)
+        B, P, L, D, S = cfg.batch, cfg.prompt_len, cfg.gen_len, cfg.block, cfg.sub_block
+        cap = cfg.cap
+        self.w_host = synth.weights(cfg, seed) if w_host is None else w_host
+        self.w = self.w_host.to(dev)
+        self.prompt = self.inp.prompt.to(dev)
+        self.boost_tok = self.inp.boost_tok.to(dev)
+        self.boost_val = self.inp.boost_val.to(dev)
+        self.tau = self.inp.tau.to(dev)
+        dt = cfg.torch_dtype
+        self.k_cache = torch.zeros((B, cfg.n_kv_heads, cap, cfg.head_dim), dtype=dt, device=dev)
+        self.v_cache = torch.zeros_like(self.k_cache)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.len = torch.zeros((B,), **i32)
+        self.tokens = torch.zeros((B, cap), **i32)
+        self.masked = torch.zeros((B, cap), dtype=torch.uint8, device=dev)
+        self.seq_steps = torch.zeros((B,), **i32)
+        self.eos_block = torch.zeros((B,), **i32)
+        self.counters = torch.zeros((2,), **i32)
+        self.slots = fdl.fdl_decode_step_slots(self.dims, self.mode, k, max_blocks)
+        self.trace = None
+        if trace:
+            T = self.slots
+            self.trace = dict(meta=torch.zeros((T, 2), **i32), tokens=torch.zeros((T, B, D), **i32),
+                              masked=torch.zeros((T, B, D), dtype=torch.uint8, device=dev),
+                              token=torch.zeros((T, B, S), **i32),
+                              conf=torch.zeros((T, B, S), dtype=torch.float32, device=dev))
+        ws = fdl.fdl_decode_workspace_size(self.dims)
+        self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
+
+    def run(self, stream=None):
+        fdl.fdl_decode(self.dims, self.w, self.prompt, self.boost_tok, self.boost_val, self.tau, self.mode, self.k,
+                       self.factor, self.inp.mask_id, self.inp.eos_id, self.inp.gain, self.max_blocks,
+                       self.k_cache, self.v_cache, self.len, self.tokens, self.masked, self.seq_steps,
+                       self.eos_block, self.counters, self.trace, self.ws, stream)
+
+    def results(self) -> dict:
+        """Host copies of the outputs; the trace as a list of per-step dicts."""
+        c = self.counters.cpu().numpy()
+        out = dict(tokens=self.tokens.cpu().numpy(), masked=self.masked.cpu().numpy(),
+                   k_cache=self.k_cache.float().cpu().numpy(), v_cache=self.v_cache.float().cpu().numpy(),
+                   length=self.len.cpu().numpy(), seq_steps=self.seq_steps.cpu().numpy(),
+                   eos_block=self.eos_block.cpu().numpy(), steps=int(c[0]), blocks_run=int(c[1]), trace=[])
+        if self.trace is not None:
+            n = min(int(c[0]), self.slots)
+            t = {name: v[:n].cpu().numpy() for name, v in self.trace.items()}
+            for s in range(n):
+                out["trace"].append(dict(block=int(t["meta"][s, 0]), sub=int(t["meta"][s, 1]),
+                                         tokens=t["tokens"][s], masked=t["masked"][s].astype(bool),
+                                         token=t["token"][s], conf=t["conf"][s]))
+        return out

@@ -10,7 +10,9 @@
  *   fdl_conf_select  greedy token, confidence, commit set per sequence
  *   fdl_kv_append    append a finished block's K/V to the cache
  * fdl_lm_head_select runs the second and third as one pass that never
- * materializes the logits.
+ * materializes the logits.  fdl_prefill_attn is the multi-block attention of
+ * the prompt prefill and of the v1 cache refresh; fdl_decode runs a whole
+ * generation (steps, sub-blocks, blocks, EOS) with its control on the device.
  *
  * Pages defining the operations (cited by title and section):
  *   "Fast-dLLM v2: Efficient Block-Diffusion LLM" (technical breakdown):
@@ -229,6 +231,90 @@ int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x
  *                    (no write, len unchanged). */
 int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new,
                   const void* v_new, int32_t n_new, int32_t* len, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode loop: a whole generation of a batch, with every control decision
+ * taken on the device.
+ *
+ * "Fast-dLLM v2", Inference Pipeline: blocks are generated left to right
+ * (Level 1); each starts fully masked and is refined sub-block by sub-block,
+ * step after step, until no position is masked (Level 2, and "Sub-block size
+ * as a decoding granularity knob"); a finished block's K/V enter the
+ * block-level cache (Level 3); generation stops once a finished block holds
+ * EOS or after max_blocks.  "Batch decoding with length padding": the batch
+ * advances in lock step; a sequence that has produced EOS gets padding blocks
+ * (MASK tokens that are never candidates).  In FDL_ATTN_DUAL_CACHE mode the
+ * cache is instead refreshed (rewritten for all P + L positions) at the start
+ * of every block and the block also attends to the cached suffix (Fast-dLLM
+ * section 3, Algorithm 1).
+ *
+ * The host enqueues a fixed schedule -- for every block and sub-block, as
+ * many step slots as the selection rule can need (sub_block for THRESHOLD
+ * and FACTOR, ceil(sub_block / k) for TOPK, since every step commits at least
+ * one masked row of every sequence that has one) -- and nothing is read back:
+ * a small control kernel before each slot opens or closes a device-side gate,
+ * and every kernel of a slot whose gate is closed returns at once.
+ *
+ * The transformer is replaced by a synthetic stand-in so that every input of
+ * a step is a function of the current tokens (w doubles as the tied token
+ * embedding; H must equal n_q_heads * head_dim):
+ *   e(t) = sqrt(H) * w[t];  query of head h = e(t)[h*d .. h*d+d);
+ *   key of KV head g = e(t)[g*d .. g*d+d);
+ *   value of KV head g = e(t)[H-(Hkv-g)*d .. H-(Hkv-g-1)*d) in reverse order;
+ *   hidden row of active position p = gain * (attention output, heads
+ *     concatenated) + boost_val[p] * w[boost_tok[p]] / |w[boost_tok[p]]|^2,
+ *     rounded to dtype;
+ *   row i of the active sub-block predicts its own position.
+ * Each step is then: embed -> fdl_block_attn -> hidden rows ->
+ * fdl_lm_head_select (with the commit update in place) on the active rows.
+ */
+typedef struct {
+  /* stand-in model */
+  const void* w;              /* [V][H] dtype: LM-head weight and tied embedding     */
+  float gain;                 /* weight of the attention output in the hidden row    */
+  int32_t mask_id, eos_id;    /* reserved ids, 0 <= id < V                            */
+  /* inputs (device) */
+  const int32_t* prompt;      /* [B][P] token ids (ids outside [0, V) read as mask_id)  */
+  const int32_t* boost_tok;   /* [B][L] drawn token per generated position (outside
+                                 [0, V): no boost)                                      */
+  const float* boost_val;     /* [B][L] its boost                                      */
+  const float* tau;           /* [B] threshold (THRESHOLD; may be NULL otherwise)      */
+  int32_t mode, k;            /* fdl_select_mode; k >= 1 for TOPK                      */
+  float factor;               /* > 0 for FACTOR                                        */
+  int32_t max_blocks;         /* 1 .. L/D; 0 = L/D                                     */
+  /* state and outputs (device, written) */
+  void* k_cache;              /* [B][Hkv][P+L][d] dtype                                */
+  void* v_cache;              /* [B][Hkv][P+L][d] dtype                                */
+  int32_t* len;               /* [B] valid cache positions at the end                  */
+  int32_t* tokens;            /* [B][P+L] prompt, generated tokens, MASK padding       */
+  uint8_t* masked;            /* [B][P+L] 1 = still masked (all 0 at the end)          */
+  int32_t* seq_steps;         /* [B] steps in which the sequence had a masked row      */
+  int32_t* eos_block;         /* [B] block whose completion stopped the sequence, -1   */
+  int32_t* counters;          /* [2] steps run, blocks run                             */
+  /* optional per-step trace: all NULL, or all set with trace_cap >= the number
+     of step slots; entry t is the t-th step that ran */
+  int32_t trace_cap;
+  int32_t* trace_meta;        /* [trace_cap][2] block, sub-block                       */
+  int32_t* trace_tokens;      /* [trace_cap][B][D] the block's tokens after the step   */
+  uint8_t* trace_masked;      /* [trace_cap][B][D] the block's masked flags after it   */
+  int32_t* trace_token;       /* [trace_cap][B][S] argmax of every active row          */
+  float* trace_conf;          /* [trace_cap][B][S] its confidence                      */
+} fdl_decode_args;
+
+/* Bytes of device workspace fdl_decode needs for dims.  0 for invalid dims. */
+size_t fdl_decode_workspace_size(const fdl_dims* dims);
+
+/* Number of step slots fdl_decode enqueues for these arguments (the trace
+ * capacity it needs); 0 for invalid arguments. */
+int32_t fdl_decode_step_slots(const fdl_dims* dims, int32_t mode, int32_t k, int32_t max_blocks);
+
+/* Run the decode loop.  dims and args are host pointers read during the
+ * call.  Requirements beyond fdl_block_attn / fdl_lm_head_select: hidden ==
+ * n_q_heads * head_dim; the workspace is fdl_decode_workspace_size(dims)
+ * bytes.  Everything is enqueued on stream; the call returns before the
+ * device finishes and reads nothing back. */
+int fdl_decode(const fdl_dims* dims, const fdl_decode_args* args, void* workspace,
+               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -114,3 +114,54 @@ def test_entry_points_reject_before_launch(L):
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 0, fake, None) == -1
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 1537, fake, None) == -1
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 32, None, None) == -1
+
+
+def _decode_args(**over):
+    fake = 16
+    a = fdl.fdl_decode_args(w=fake, gain=2.0, mask_id=10, eos_id=11, prompt=fake, boost_tok=fake, boost_val=fake,
+                            tau=fake, mode=0, k=0, factor=1.0, max_blocks=0, k_cache=fake, v_cache=fake, len=fake,
+                            tokens=fake, masked=fake, seq_steps=fake, eos_block=fake, counters=fake, trace_cap=0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_slots_and_workspace(L):
+    d = _dims()
+    nb, subs, S = 512 // 32, 32 // 8, 8
+    assert fdl.fdl_decode_step_slots(d, fdl.FDL_SELECT_THRESHOLD, 0, 0) == nb * subs * S
+    assert fdl.fdl_decode_step_slots(d, fdl.FDL_SELECT_FACTOR, 0, 2) == 2 * subs * S
+    assert fdl.fdl_decode_step_slots(d, fdl.FDL_SELECT_TOPK, 3, 1) == subs * 3
+    assert fdl.fdl_decode_step_slots(d, fdl.FDL_SELECT_TOPK, 0, 1) == 0
+    assert fdl.fdl_decode_step_slots(d, fdl.FDL_SELECT_THRESHOLD, 0, nb + 1) == 0
+    ws = fdl.fdl_decode_workspace_size(d)
+    assert ws >= fdl.fdl_block_attn_workspace_size(d) + fdl.fdl_lm_head_select_workspace_size(d, 8)
+    assert fdl.fdl_decode_workspace_size(_dims(batch=0)) == 0
+
+
+def test_decode_rejects_before_launch(L):
+    d = _dims()
+    by = ctypes.byref
+    ws = fdl.fdl_decode_workspace_size(d)
+    fake = ctypes.c_void_p(16)
+
+    def call(dims=d, args=None, wsz=ws, w=fake):
+        return L.fdl_decode(by(dims), by(args if args is not None else _decode_args()), w, wsz, None)
+
+    assert L.fdl_decode(by(d), None, fake, ws, None) == -1
+    assert call(args=_decode_args(w=None)) == -1
+    assert call(args=_decode_args(prompt=None)) == -1
+    assert call(args=_decode_args(mask_id=152064)) == -1
+    assert call(args=_decode_args(eos_id=-1)) == -1
+    assert call(args=_decode_args(gain=float("nan"))) == -1
+    assert call(args=_decode_args(max_blocks=17)) == -1
+    assert call(args=_decode_args(tau=None)) == -1
+    assert call(args=_decode_args(mode=1, k=0)) == -1
+    assert call(args=_decode_args(mode=2, factor=0.0)) == -1
+    assert call(args=_decode_args(trace_meta=16)) == -1           # trace pointers: all or none
+    full = dict(trace_meta=16, trace_tokens=16, trace_masked=16, trace_token=16, trace_conf=16)
+    slots = fdl.fdl_decode_step_slots(d, 0, 0, 0)
+    assert call(args=_decode_args(trace_cap=slots - 1, **full)) == -1
+    assert call(dims=_dims(hidden=3520)) == -2                    # stand-in model needs H = Hq * d
+    assert call(wsz=ws - 1) == -4
+    assert call(w=None) == -4
