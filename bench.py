@@ -1,6 +1,7 @@
 """Benchmark: cached block-diffusion denoising steps on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --decode-loop [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch: block attention over
 the prefix cache + block, LM head, confidence select (with the commit-state
@@ -9,6 +10,12 @@ workload is the Qwen2.5-7B-shaped one (batch 4, 28/4 heads, d 128, prompt
 1024, answer 512, block 32, sub-block 8, vocab 152064, tau 0.9); its 64-step
 schedule is replayed until K steps have been timed.  Inputs are resident in
 HBM before timing starts.  Prints one JSON line.
+
+With --decode-loop a timed unit is instead one whole generation of the batch
+through fdl_decode (the device-side decode loop with its stand-in model):
+every block, sub-block and step until all positions are committed or EOS
+stops the sequences; K generations are timed after W warmup generations, and
+the line reports steps/s and committed tokens/s of those generations.
 """
 from __future__ import annotations
 
@@ -101,6 +108,83 @@ def cpu_baseline(run, budget_s: float):
                       f"select, append), {dt:.1f} s; {commits / dt:.3f} committed tokens/s"}
 
 
+def attn_bytes(cfg, lk: int) -> int:
+    """Algorithmic bytes of one attention call: Q and O once, every visible
+    K/V row of every KV head once."""
+    esz = 4 if cfg.dtype == "f32" else 2
+    qo = 2 * cfg.batch * cfg.sub_block * cfg.n_q_heads * cfg.head_dim * esz
+    return qo + 2 * cfg.batch * cfg.n_kv_heads * lk * cfg.head_dim * esz
+
+
+def bench_decode_loop(args, cfg):
+    import numpy as np
+    import torch
+    from block_diffusion_decoding_attn_amd.runner import DecodeRunner
+
+    run = DecodeRunner(cfg, select=args.select, k=args.k, boost=args.boost, trace=True)
+    for _ in range(max(args.warmup, 1)):
+        run.run()
+    torch.cuda.synchronize()
+    res = run.results()
+    steps = res["steps"]
+    # committed positions: every position of the blocks a sequence generated
+    committed = int(sum((res["eos_block"][b] + 1 if res["eos_block"][b] >= 0 else res["blocks_run"]) * cfg.block
+                        for b in range(cfg.batch)))
+    # algorithmic HBM bytes of the steps that ran: LM head + attention
+    lm_b, _ = lm_head_bytes_flops(cfg, True)
+    att_b = 0
+    for t in res["trace"]:
+        lp = cfg.prompt_len + t["block"] * cfg.block
+        lk = cfg.cap if cfg.attn_mode == "dual_cache" else lp + cfg.block
+        att_b += attn_bytes(cfg, lk)
+    byts = steps * lm_b + att_b
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    host = []
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        h = time.perf_counter()
+        run.run(trace=False)
+        host.append(time.perf_counter() - h)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    if int(run.counters[0]) != steps:
+        raise RuntimeError("the timed generations ran a different number of steps")
+    achieved = byts / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": steps / (ms * 1e-3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} decode loop", "batch": cfg.batch, "prompt_len": cfg.prompt_len,
+                   "gen_len": cfg.gen_len, "block": cfg.block, "sub_block": cfg.sub_block, "hidden": cfg.hidden,
+                   "vocab": cfg.vocab, "attn_mode": cfg.attn_mode, "select": args.select, "tau": list(cfg.tau),
+                   "gain": run.inp.gain, "timed_unit": "one generation (fdl_decode call)",
+                   "parallelism": "single-gpu"},
+        "committed_tokens_per_s": committed / (ms * 1e-3),
+        "ms_per_generation": ms,
+        "steps_per_generation": steps,
+        "step_slots_enqueued": run.slots,
+        "blocks_run": res["blocks_run"],
+        "eos_block": [int(x) for x in res["eos_block"]],
+        "host_enqueue_ms": 1e3 * float(np.median(host)),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "whole loop: LM head + attention algorithmic bytes of the steps run / loop time",
+                     "algorithmic_bytes": byts},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +198,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="fdl_lm_head + fdl_conf_select (logits materialized) instead of fdl_lm_head_select")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="time whole generations through fdl_decode instead of single steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -129,6 +215,9 @@ def main():
         sys.exit(1)
     fdl.lib()
     cfg = synth.get_config(args.workload)
+    if args.decode_loop:
+        bench_decode_loop(args, cfg)
+        return
     t_setup = time.perf_counter()
     run = StepRunner(cfg, select=args.select, k=args.k, boost=args.boost, keep_host=not args.no_cpu_baseline,
                      fused=not args.unfused)

@@ -10,8 +10,9 @@
 //     stream: W is read once with coalesced 16-byte non-temporal loads,
 //     staged with the matching X slab through LDS, and fed to MFMA
 //     (A = W rows, B = X^T).
-//   * tiled (M > 64): MFMA-bound; 128 x 128 output tiles per workgroup, K
-//     staged through LDS in 64-wide slabs, 32x32x16 bf16 MFMA.
+//   * tiled (M > 64): MFMA-bound; 256 x 256 output tiles per workgroup, K
+//     streamed HBM -> LDS by direct-to-LDS loads through a 4-stage ring,
+//     32x32x16 bf16 MFMA.
 #include "common.h"
 
 namespace fdl {
@@ -236,14 +237,33 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// tiled: workgroup tile 128 (vocab) x 128 (rows), 4 waves of 64 x 64, K slabs
-// of 64 through LDS with the next slab prefetched into registers.
-constexpr int TB_V = 128, TB_M = 128, TB_K = 64, TB_PAD = 8, TB_ST = TB_K + TB_PAD;
+// tiled (M > 64): workgroup tile 256 (vocab) x 256 (rows), 8 waves in a 2 x 4
+// grid of 128 x 64 wave tiles (4 x 2 MFMA 32x32x16 tiles each).  K is consumed
+// in 32-wide slabs that travel HBM -> LDS by global_load_lds_dwordx4 (no
+// register staging, so the loads can run TB_NST - 1 slabs ahead of the MFMA
+// work at one workgroup per CU) through a TB_NST-stage ring.  A slab row is
+// 64 bytes = 4 chunks of 16; chunk c of row r sits at chunk c ^ ((r >> 2) & 3)
+// so that the 32-row fragment reads of a wave are free of bank conflicts.
+constexpr int TB_V = 256, TB_M = 256, TB_K = 32, TB_NST = 4, TB_NWV = 2, TB_NWM = 4;
+constexpr int TB_ROWB = TB_K * 2;                          // bytes per row per stage
+constexpr int TB_ABYTES = TB_V * TB_ROWB, TB_STB = (TB_V + TB_M) * TB_ROWB;
+constexpr int TB_NT = TB_NWV * TB_NWM * 64;
+constexpr int TB_IPW = TB_STB / 1024 / (TB_NWV * TB_NWM);  // 1 KB load instructions per wave per stage
+constexpr int TB_TV = TB_V / TB_NWV / 32, TB_TM = TB_M / TB_NWM / 32;
+static_assert(TB_TV * 32 == 128, "a wave covers one 128-row vocabulary tile of the select partials");
 
-__global__ __launch_bounds__(256) void lm_head_tiled_bf16(LmArgs a) {
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((((N >> 4) & 3) << 14) | (0xF << 8) | (7 << 4) | (N & 15));
+}
+
+__global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
   if (gate_closed(a.gate)) return;
-  __shared__ __attribute__((aligned(16))) bf16_t As[TB_V * TB_ST];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[TB_M * TB_ST];
+  __shared__ __attribute__((aligned(1024))) char smem[TB_NST * TB_STB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
@@ -255,105 +275,116 @@ __global__ __launch_bounds__(256) void lm_head_tiled_bf16(LmArgs a) {
   if (tile >= ntiles) return;
   const int vt = tile / nmt, mt = tile % nmt;
   const int v0 = vt * TB_V, m0 = mt * TB_M;
-  const int wv = (wave & 1) * 64, wm = (wave >> 1) * 64;
+  const int wv0 = (wave % TB_NWV) * (TB_TV * 32), wm0 = (wave / TB_NWV) * (TB_TM * 32);
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
 
-  // each thread stages 4 chunks of A and 4 of B per slab (128 rows x 8 chunks)
-  const bf16_t* ap[4];
-  const bf16_t* bp[4];
-  bool bok[4];
-  int srow[4], scol[4];
+  // Load instruction j of this wave fills stage bytes [kb KB, kb KB + 1 KB),
+  // 16 rows (W rows 0..255, then X rows): lane l writes physical chunk l & 3
+  // of row kb * 16 + l / 4, which holds logical chunk (l & 3) ^ ((row >> 2) & 3).
+  // Rows past V or M read a valid row; their results are never stored.
+  const bf16_t* src[TB_IPW];
+  int dst[TB_IPW];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int ch = tid + c * 256;
-    srow[c] = ch >> 3;
-    scol[c] = (ch & 7) * 8;
-    int vr = v0 + srow[c];
-    vr = vr < a.V ? vr : a.V - 1;
-    ap[c] = W + size_t(vr) * a.H + scol[c];
-    const int mr = m0 + srow[c];
-    bok[c] = mr < a.M;
-    bp[c] = X + size_t(bok[c] ? mr : 0) * a.H + scol[c];
+  for (int j = 0; j < TB_IPW; ++j) {
+    const int kb = wave * TB_IPW + j;
+    const int rr = kb * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((rr >> 2) & 3);
+    if (rr < TB_V) src[j] = W + size_t(min(v0 + rr, a.V - 1)) * a.H + c * 8;
+    else src[j] = X + size_t(min(m0 + rr - TB_V, a.M - 1)) * a.H + c * 8;
+    dst[j] = kb * 1024;
   }
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int k) {
+  auto issue = [&](int slab) {
+    char* sb = smem + (slab % TB_NST) * TB_STB;
+    const int k0 = slab * TB_K;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      ra[c] = ld16(ap[c] + k);
-      rb[c] = bok[c] ? ld16(bp[c] + k) : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < TB_IPW; ++j)
+      __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_void_t*)(sb + dst[j]), 16, 0, 0);
   };
-  f32x16 acc[2][2];
+
+  f32x16 acc[TB_TV][TB_TM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TB_TV; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TB_TM; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  gload(0);
-  for (int k = 0; k < a.H; k += TB_K) {
+  const int nk = a.H / TB_K;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      *reinterpret_cast<u32x4*>(&As[srow[c] * TB_ST + scol[c]]) = ra[c];
-      *reinterpret_cast<u32x4*>(&Bs[srow[c] * TB_ST + scol[c]]) = rb[c];
-    }
-    __syncthreads();
-    if (k + TB_K < a.H) gload(k + TB_K);
+  for (int s = 0; s < TB_NST - 1; ++s)
+    if (s < nk) issue(s);
+  for (int t = 0; t < nk; ++t) {
+    // this wave's loads of slab t have landed once at most the later slabs'
+    // loads are in flight; after the barrier every wave's have
+    if (t + TB_NST - 2 < nk) wait_vmcnt<(TB_NST - 2) * TB_IPW>();
+    else wait_vmcnt<0>();
+    // a bare barrier: __syncthreads() would also wait for the loads still in flight
+    __builtin_amdgcn_s_barrier();
+    // the buffer refilled here held slab t - 1, which every wave has finished
+    if (t + TB_NST - 1 < nk) issue(t + TB_NST - 1);
+    const char* sb = smem + (t % TB_NST) * TB_STB;
+    const bf16_t* As = reinterpret_cast<const bf16_t*>(sb);
+    const bf16_t* Bs = reinterpret_cast<const bf16_t*>(sb + TB_ABYTES);
+    u32x4 af[2][TB_TV], bf[2][TB_TM];
+    auto frag = [&](int ks, int p) {
+      const int c = 2 * ks + half;
 #pragma unroll
-    for (int kk = 0; kk < TB_K; kk += 16) {
-      u32x4 af[2], bf[2];
+      for (int i = 0; i < TB_TV; ++i) {
+        const int r = wv0 + i * 32 + l32;
+        af[p][i] = *reinterpret_cast<const u32x4*>(As + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
+      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(&As[(wv + i * 32 + l32) * TB_ST + kk + 8 * half]);
+      for (int j = 0; j < TB_TM; ++j) {
+        const int r = wm0 + j * 32 + l32;
+        bf[p][j] = *reinterpret_cast<const u32x4*>(Bs + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
+      }
+    };
+    auto mma = [&](int p) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(&Bs[(wm + j * 32 + l32) * TB_ST + kk + 8 * half]);
+      for (int i = 0; i < TB_TV; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                              __builtin_bit_cast(bf16x8, bf[j]), acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+        for (int j = 0; j < TB_TM; ++j) acc[i][j] = mfma32x32x16_bf16(af[p][i], bf[p][j], acc[i][j]);
+    };
+    // both k-steps' fragments are read before the MFMAs of the first start
+    frag(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    frag(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
   }
-  // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile
-  if (a.part) {
-    // per row: over the lane's 32 vocabulary rows (increasing), the other
-    // half-wave, then the two waves sharing the rows
-    __shared__ f32x4 red[2][TB_M];
+
+  // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile; a
+  // wave's 128 vocabulary rows are exactly one tile of the select partials
+  if (a.part && v0 + wv0 < a.V) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TB_TM; ++j) {
       Red r = red_empty();
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TB_TV; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int v = v0 + wv + i * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+          const int v = v0 + wv0 + i * 32 + (e / 4) * 8 + half * 4 + (e % 4);
           if (v < a.V) push(r, acc[i][j][e], v);
         }
       r = combine(r, shfl_xor_red(r, 32));
-      if (half == 0) red[wave & 1][wm + j * 32 + l32] = pack_red(r);
-    }
-    __syncthreads();
-    if (tid < TB_M && m0 + tid < a.M) {
-      const Red r = combine(unpack_red(red[0][tid]), unpack_red(red[1][tid]));
-      a.part[size_t(m0 + tid) * a.nc + vt] = pack_red(r);
+      const int m = m0 + wm0 + j * 32 + l32;
+      if (half == 0 && m < a.M) a.part[size_t(m) * a.nc + (v0 + wv0) / 128] = pack_red(r);
     }
   }
   if (!a.out) return;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + wm + j * 32 + l32;
+  for (int j = 0; j < TB_TM; ++j) {
+    const int m = m0 + wm0 + j * 32 + l32;
     if (m >= a.M) continue;
     float* orow = a.out + size_t(m) * a.V;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TB_TV; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int v = v0 + wv + i * 32 + q * 8 + half * 4;
+        const int v = v0 + wv0 + i * 32 + q * 8 + half * 4;
         const f32x4 val{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         if (v + 3 < a.V && (a.V & 3) == 0) {
           *reinterpret_cast<f32x4*>(orow + v) = val;
@@ -397,7 +428,7 @@ int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, fl
       case 4: launch_skinny_bf16<4>(a, st); break;
       default: {
         const int nvt = (a.V + TB_V - 1) / TB_V, nmt = (rows + TB_M - 1) / TB_M;
-        hipLaunchKernelGGL(lm_head_tiled_bf16, dim3(8 * ((nvt * nmt + 7) / 8)), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(lm_head_tiled_bf16, dim3(8 * ((nvt * nmt + 7) / 8)), dim3(TB_NT), 0, st, a);
       }
     }
   } else {

@@ -205,11 +205,12 @@ class DecodeRunner:
         ws = fdl.fdl_decode_workspace_size(self.dims)
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
 
-    def run(self, stream=None):
+    def run(self, stream=None, trace: bool = True):
+        """Enqueue one whole generation; trace=False skips the per-step record."""
         fdl.fdl_decode(self.dims, self.w, self.prompt, self.boost_tok, self.boost_val, self.tau, self.mode, self.k,
                        self.factor, self.inp.mask_id, self.inp.eos_id, self.inp.gain, self.max_blocks,
                        self.k_cache, self.v_cache, self.len, self.tokens, self.masked, self.seq_steps,
-                       self.eos_block, self.counters, self.trace, self.ws, stream)
+                       self.eos_block, self.counters, self.trace if trace else None, self.ws, stream)
 
     def results(self) -> dict:
         """Host copies of the outputs; the trace as a list of per-step dicts."""
