@@ -449,16 +449,17 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
     if (j >= lp && j < lp + a.D) return blk + size_t(j - lp) * DH;
     return cache + size_t(j) * DH;
   };
-  u32x4 kreg[KCH_T];
-  u32x4 vreg[VU_T][4];
-  auto load_tile = [&](int key0) {
+  // two register stages: tile t + 2 is fetched while tile t is computed
+  u32x4 kreg[2][KCH_T];
+  u32x4 vreg[2][VU_T][4];
+  auto load_tile = [&](int rs, int key0) {
 #pragma unroll
     for (int c = 0; c < KCH_T; ++c) {
       const int ch = tid + c * NT;
-      kreg[c] = u32x4{0, 0, 0, 0};
+      kreg[rs][c] = u32x4{0, 0, 0, 0};
       if (ch < KCH) {
         const int key = key0 + ch / CPR;
-        if (key < k_end) kreg[c] = ld16(key_ptr(kc, kbk, key) + (ch % CPR) * EPC);
+        if (key < k_end) kreg[rs][c] = ld16(key_ptr(kc, kbk, key) + (ch % CPR) * EPC);
       }
     }
 #pragma unroll
@@ -466,19 +467,19 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
       const int un = tid + u * NT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vreg[u][e] = u32x4{0, 0, 0, 0};
+        vreg[rs][u][e] = u32x4{0, 0, 0, 0};
         if (un < VU) {
           const int key = key0 + (un % (TK / 4)) * 4 + e;
-          if (key < k_end) vreg[u][e] = ld16(key_ptr(vc, vbk, key) + (un / (TK / 4)) * EPC);
+          if (key < k_end) vreg[rs][u][e] = ld16(key_ptr(vc, vbk, key) + (un / (TK / 4)) * EPC);
         }
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int rs, int buf) {
 #pragma unroll
     for (int c = 0; c < KCH_T; ++c) {
       const int ch = tid + c * NT;
-      if (ch < KCH) *reinterpret_cast<u32x4*>(&Ks[buf][(ch / CPR) * KST + (ch % CPR) * EPC]) = kreg[c];
+      if (ch < KCH) *reinterpret_cast<u32x4*>(&Ks[buf][(ch / CPR) * KST + (ch % CPR) * EPC]) = kreg[rs][c];
     }
 #pragma unroll
     for (int u = 0; u < VU_T; ++u) {
@@ -486,10 +487,10 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
       if (un >= VU) continue;
       const int k4 = (un % (TK / 4)) * 4;
       const int d0 = (un / (TK / 4)) * EPC;
-      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&vreg[u][0]);
-      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&vreg[u][1]);
-      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&vreg[u][2]);
-      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&vreg[u][3]);
+      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][0]);
+      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][1]);
+      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][2]);
+      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][3]);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         u32x2 w;
@@ -582,16 +583,25 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
       }
   };
 
+  // tile t lives in register stage t & 1 until it is stored to LDS buffer
+  // t & 1; its load is issued two tiles ahead of its use, so two tiles of
+  // MFMA work cover its latency
   const int ntiles = (k_end - k_begin + TK - 1) / TK;
-  load_tile(k_begin);
-  store_tile(0);
+  load_tile(0, k_begin);
+  if (ntiles > 1) load_tile(1, k_begin + TK);
+  store_tile(0, 0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(k_begin + (t + 1) * TK);
+  // the stage index is a literal at each call (register arrays cannot be
+  // indexed at run time without going to scratch), hence the loop by two
+  auto step = [&](int t, int buf) {
+    if (t + 2 < ntiles) load_tile(buf, k_begin + (t + 2) * TK);  // stage buf held tile t, already in LDS
     compute_tile(buf, k_begin + t * TK);
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    if (t + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, 0);
+    if (t + 1 < ntiles) step(t + 1, 1);
   }
   // epilogue: o[j][dt][v] = O^T[d = 32dt + 8(v/4) + 4h + v%4][query l32]
 #pragma unroll
@@ -628,30 +638,24 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
 }
 
 
-// Merge the split partials of every query row in split order.  Loads are
-// issued eight splits at a time so that their latencies overlap (the partials
-// were written by workgroups on other XCDs and come back from beyond L2).
+// Merge the split partials of every query row in split order.  The loads of
+// up to sixteen splits are issued together so that their latencies overlap
+// (the partials were written by workgroups on other XCDs and come back from
+// beyond L2): one round of memory latency for the usual split counts.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void block_attn_merge_kernel(AttnArgs a) {
   if (gate_closed(a.gate)) return;
   constexpr int TPR = DH / 4;  // threads per row, 4 dims each
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int n_rows = a.B * a.Hq * a.S;
   const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int d0 = (threadIdx.x % TPR) * 4;
   if (row >= n_rows) return;
   const size_t stride = size_t(n_rows);
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
-  float mmax = -INFINITY;
-  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
-    float2 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = s0 + u < a.nsplit ? ml[(s0 + u) * stride + row] : float2{-INFINITY, 0.f};
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (v[u].y > 0.f) mmax = fmaxf(mmax, v[u].x);
-  }
-  float lsum = 0.f;
+  // splits in rounds of U (one round for U or fewer splits), each round's
+  // loads issued together; across rounds the reference maximum is carried
+  float mmax = -INFINITY, lsum = 0.f;
   f32x4 acc{0, 0, 0, 0};
   for (int s0 = 0; s0 < a.nsplit; s0 += U) {
     float2 v[U];
@@ -662,6 +666,16 @@ __global__ __launch_bounds__(256) void block_attn_merge_kernel(AttnArgs a) {
       v[u] = ok ? ml[(s0 + u) * stride + row] : float2{-INFINITY, 0.f};
       po[u] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + ((s0 + u) * stride + row) * DH + d0)
                  : f32x4{0, 0, 0, 0};
+    }
+    float rmax = mmax;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v[u].y > 0.f) rmax = fmaxf(rmax, v[u].x);
+    if (rmax > mmax) {
+      const float alpha = mmax == -INFINITY ? 0.f : exp2f(mmax - rmax);
+      lsum *= alpha;
+      acc *= alpha;
+      mmax = rmax;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -329,7 +329,7 @@ static DecLayout decode_layout(const fdl_dims& d) {
   L.vb = take(size_t(d.batch) * d.n_kv_heads * d.block * d.head_dim * es);
   L.o = take(rows * d.hidden * es);
   L.x = take(rows * d.hidden * es);
-  L.part = take(rows * size_t(lm_head_tiles(d)) * 16);
+  L.part = take(partials_workspace_bytes(d, d.sub_block, lm_head_tiles(d)));
   L.attn = take(attn_workspace_bytes(d));
   L.tok = take(rows * sizeof(int32_t));
   L.conf = take(rows * sizeof(float));

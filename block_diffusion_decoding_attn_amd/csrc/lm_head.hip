@@ -14,6 +14,7 @@
 //     streamed HBM -> LDS by direct-to-LDS loads through a 4-stage ring,
 //     32x32x16 bf16 MFMA.
 #include "common.h"
+#include "launch.h"
 
 namespace fdl {
 
@@ -24,7 +25,16 @@ struct LmArgs {
   f32x4* part;   // [M][nc] confidence partials per 128-row vocabulary tile, or null
   int M, H, V, nc;
   const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
+  int32_t* cnt;         // select row counters to zero (with part), or null
+  int ncnt;
 };
+
+// Workgroup 0 zeroes the select's per-sequence row counters for the
+// finalize kernel that follows on the stream.
+__device__ __forceinline__ void zero_counters(const LmArgs& a) {
+  if (a.cnt && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.ncnt; i += blockDim.x) a.cnt[i] = 0;
+}
 
 // Fused-select epilogue, shared by the skinny kernels: lane holds
 // acc[t][n][e] = logit of vocabulary row vbase + 16t + 4grp + e for column
@@ -71,6 +81,7 @@ __device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (
 template <int NTM, int ROWS, int KSLAB, int WPB>
 __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
   if (gate_closed(a.gate)) return;
+  zero_counters(a);
   constexpr int NT = WPB * 64;
   constexpr int CPR = KSLAB * 2 / 16;        // 16-byte chunks per row of a slab
   constexpr int WCH = ROWS * CPR;            // W chunks per slab
@@ -189,6 +200,7 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
 template <int NTM, int RT>
 __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
   if (gate_closed(a.gate)) return;
+  zero_counters(a);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int v0 = (blockIdx.x * 4 + wave) * RT * 16;
@@ -263,6 +275,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
   if (gate_closed(a.gate)) return;
+  zero_counters(a);
   __shared__ __attribute__((aligned(1024))) char smem[TB_NST * TB_STB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -418,7 +431,12 @@ int lm_head_tiles(const fdl_dims& d) { return (d.vocab + 127) / 128; }
 
 int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
                    hipStream_t st, const int32_t* gate) {
-  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d), gate};
+  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d), gate,
+           nullptr, 0};
+  if (part) {
+    a.cnt = partials_counters(part, d, rows / d.batch, a.nc);
+    a.ncnt = d.batch;
+  }
   const int ntm = (rows + 15) / 16;
   if (d.dtype == FDL_BF16) {
     switch (ntm) {

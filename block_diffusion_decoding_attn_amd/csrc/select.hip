@@ -37,12 +37,15 @@ struct SelArgs {
   int B, R, V, NC, chunk;
   int sstride;          // elements between sequences in masked / tokens_inout / masked_inout
   const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
+  int32_t* cnt;         // [B] rows finalized per sequence (zeroed by the producer of the partials)
 };
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void select_partial_kernel(SelArgs a) {
   __shared__ Red sh[4];
   if (gate_closed(a.gate)) return;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < a.B; i += 256) a.cnt[i] = 0;
   const int row = blockIdx.y, c = blockIdx.x;
   const int v_begin = c * a.chunk;
   const int v_end = min(v_begin + a.chunk, a.V);
@@ -75,47 +78,59 @@ __global__ __launch_bounds__(256) void select_partial_kernel(SelArgs a) {
   }
 }
 
-// One workgroup of 1024 threads per sequence.  Phase 1: the chunk partials
-// of row r are merged by TPR = min(64, 1024 / R') threads (R' = R rounded up
-// to a power of two) that each take chunks j, j+TPR, ... in increasing order,
-// eight independent loads at a time, followed by a fixed butterfly over the
-// TPR lanes.  Phase 2: one thread per row (R <= 256) applies the rule.
-constexpr int FIN_NT = 1024;
+// One workgroup of FIN_NT threads per row.  Phase 1: the row's chunk
+// partials are merged, thread j taking chunks j, j + FIN_NT, ... in
+// increasing order (all its loads issued together), then a fixed butterfly
+// over the wave and a fixed-order combination of the waves: the result does
+// not depend on scheduling.  The row's token and confidence are written and
+// the row is counted for its sequence (a device-scope counter that the
+// producer kernel zeroed).  Phase 2 runs only in the workgroup that counts a
+// sequence's last row: one thread per row (R <= 256) applies the rule.
+constexpr int FIN_NT = 256;
+constexpr int FIN_U = 8;
 
 __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
+  __shared__ Red red_w[FIN_NT / 64];
   __shared__ float conf_s[256];
-  __shared__ int tok_s[256];
   __shared__ int cand_s[256];
   __shared__ int red_i[256];
+  __shared__ int last_s;
   if (gate_closed(a.gate)) return;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int rpow = 1;
-  while (rpow < a.R) rpow <<= 1;
-  const int tpr = min(64, FIN_NT / rpow);
+  const int row_g = blockIdx.x;               // b * R + r
+  const int b = row_g / a.R;
+  const int tid = threadIdx.x;
   {
-    const int rr = tid / tpr, j = tid % tpr;
+    const f32x4* prow = a.part + size_t(row_g) * a.NC;
     Red t = red_empty();
-    if (rr < a.R) {
-      const f32x4* prow = a.part + (size_t(b) * a.R + rr) * a.NC;
-      constexpr int U = 8;
-      for (int c0 = j; c0 < a.NC; c0 += tpr * U) {
-        f32x4 p[U];
+    for (int c0 = tid; c0 < a.NC; c0 += FIN_NT * FIN_U) {
+      f32x4 p[FIN_U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * tpr;
-          p[u] = c < a.NC ? prow[c] : f32x4{-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) t = combine(t, unpack_red(p[u]));
+      for (int u = 0; u < FIN_U; ++u) {
+        const int c = c0 + u * FIN_NT;
+        p[u] = c < a.NC ? prow[c] : f32x4{-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
       }
+#pragma unroll
+      for (int u = 0; u < FIN_U; ++u) t = combine(t, unpack_red(p[u]));
     }
-    for (int o = 1; o < tpr; o <<= 1) t = combine(t, shfl_xor_red(t, o));
-    if (rr < a.R && j == 0) {
-      conf_s[rr] = 1.f / t.s;
-      tok_s[rr] = t.i;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) t = combine(t, shfl_xor_red(t, o));
+    if ((tid & 63) == 0) red_w[tid >> 6] = t;
+    __syncthreads();
+    if (tid == 0) {
+      Red r = red_w[0];
+#pragma unroll
+      for (int w = 1; w < FIN_NT / 64; ++w) r = combine(r, red_w[w]);
+      a.token_out[row_g] = r.i;
+      a.conf_out[row_g] = 1.f / r.s;
+      // publish the row, then count it; the last row of the sequence applies the rule
+      __threadfence();
+      const int prev = atomicAdd(&a.cnt[b], 1);
+      last_s = prev == a.R - 1;
     }
+    __syncthreads();
+    if (!last_s) return;
+    __threadfence();
   }
-  __syncthreads();
   const int r = tid;
   const bool live = r < a.R;
   const size_t row = size_t(b) * a.R + r;
@@ -123,11 +138,10 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   float conf = 0.f;
   int tok = 0, cand = 0;
   if (live) {
-    conf = conf_s[r];
-    tok = tok_s[r];
+    conf = __hip_atomic_load(&a.conf_out[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tok = __hip_atomic_load(&a.token_out[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     cand = a.masked[srow] != 0;
-    a.token_out[row] = tok;
-    a.conf_out[row] = conf;
+    conf_s[r] = conf;
   }
   if (r < 256) cand_s[r] = live ? cand : 0;
   __syncthreads();
@@ -141,9 +155,9 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
       rank += (cq > conf || (cq == conf && q < r)) ? 1 : 0;
     }
   }
-  // block reductions over the first 256 threads (every thread reaches each barrier)
+  // block reductions (every thread reaches each barrier)
   auto reduce_sum = [&](int v) {
-    if (r < 256) red_i[r] = v;
+    red_i[r] = v;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if (r < o) red_i[r] += red_i[r + o];
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
     return out;
   };
   auto reduce_max = [&](int v) {
-    if (r < 256) red_i[r] = v;
+    red_i[r] = v;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if (r < o) red_i[r] = max(red_i[r], red_i[r + o]);
@@ -179,7 +193,10 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
     sel = live && cand && rank < nstar;
   }
   const int n_sel = reduce_sum(sel ? 1 : 0);
-  if (r == 0) a.n_commit[b] = n_sel;
+  if (r == 0) {
+    a.n_commit[b] = n_sel;
+    a.cnt[b] = 0;
+  }
   if (live) {
     a.commit_out[row] = sel ? 1 : 0;
     if (sel && a.tokens_inout) a.tokens_inout[srow] = tok;
@@ -200,10 +217,21 @@ static void select_plan(int rows, int V, int& nc, int& chunk) {
   nc = (V + chunk - 1) / chunk;
 }
 
+// Partials [B*R][nc] (16 bytes each), then the per-sequence row counters.
+size_t partials_workspace_bytes(const fdl_dims& d, int rows_per_seq, int nc) {
+  const size_t part = size_t(d.batch) * rows_per_seq * nc * sizeof(f32x4);
+  return part + (size_t(d.batch) * sizeof(int32_t) + 15) / 16 * 16;
+}
+
+int32_t* partials_counters(void* ws, const fdl_dims& d, int rows_per_seq, int nc) {
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                    size_t(d.batch) * rows_per_seq * nc * sizeof(f32x4));
+}
+
 size_t select_workspace_bytes(const fdl_dims& d, int rows_per_seq) {
   int nc, chunk;
   select_plan(d.batch * rows_per_seq, d.vocab, nc, chunk);
-  return size_t(d.batch) * rows_per_seq * nc * sizeof(f32x4);
+  return partials_workspace_bytes(d, rows_per_seq, nc);
 }
 
 // Finalize from partials produced elsewhere (the LM head's fused epilogue).
@@ -221,7 +249,8 @@ int select_finalize_launch(const fdl_dims& d, int R, const void* part, int nc, c
   a.sstride = state_stride > 0 ? state_stride : R;
   a.gate = gate;
   a.part = reinterpret_cast<f32x4*>(const_cast<void*>(part));
-  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch), dim3(FIN_NT), 0, st, a);
+  a.cnt = partials_counters(const_cast<void*>(part), d, R, nc);
+  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch * R), dim3(FIN_NT), 0, st, a);
   return check_launch();
 }
 
@@ -237,13 +266,14 @@ int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* 
   a.sstride = R;
   a.gate = nullptr;
   select_plan(d.batch * R, d.vocab, a.NC, a.chunk);
-  const size_t need = size_t(d.batch) * R * a.NC * sizeof(f32x4);
+  const size_t need = partials_workspace_bytes(d, R, a.NC);
   if (!ws || ws_bytes < need) return FDL_E_WORKSPACE;
   a.part = reinterpret_cast<f32x4*>(ws);
+  a.cnt = partials_counters(ws, d, R, a.NC);
   const dim3 grid(a.NC, d.batch * R);
   if ((d.vocab & 3) == 0) hipLaunchKernelGGL(select_partial_kernel<true>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(select_partial_kernel<false>, grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch), dim3(FIN_NT), 0, st, a);
+  hipLaunchKernelGGL(select_finalize_kernel, dim3(d.batch * R), dim3(FIN_NT), 0, st, a);
   return check_launch();
 }
 
