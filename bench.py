@@ -138,13 +138,17 @@ def bench_decode_loop(args, cfg):
         lk = cfg.cap if cfg.attn_mode == "dual_cache" else lp + cfg.block
         att_b += attn_bytes(cfg, lk)
     byts = steps * lm_b + att_b
+    graph = run.capture(trace=False) if args.graph else None
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     host = []
     torch.cuda.synchronize()
     t0.record()
     for _ in range(args.steps):
         h = time.perf_counter()
-        run.run(trace=False)
+        if graph is not None:
+            graph.replay()
+        else:
+            run.run(trace=False)
         host.append(time.perf_counter() - h)
     t1.record()
     torch.cuda.synchronize()
@@ -169,6 +173,7 @@ def bench_decode_loop(args, cfg):
                    "gen_len": cfg.gen_len, "block": cfg.block, "sub_block": cfg.sub_block, "hidden": cfg.hidden,
                    "vocab": cfg.vocab, "attn_mode": cfg.attn_mode, "select": args.select, "tau": list(cfg.tau),
                    "gain": run.inp.gain, "timed_unit": "one generation (fdl_decode call)",
+                   "launch": "hip graph replay" if args.graph else "eager enqueue",
                    "parallelism": "single-gpu"},
         "committed_tokens_per_s": committed / (ms * 1e-3),
         "ms_per_generation": ms,
@@ -200,6 +205,8 @@ def main():
                     help="fdl_lm_head + fdl_conf_select (logits materialized) instead of fdl_lm_head_select")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time whole generations through fdl_decode instead of single steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode-loop: capture the generation in a HIP graph and time its replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "

@@ -212,6 +212,21 @@ class DecodeRunner:
                        self.k_cache, self.v_cache, self.len, self.tokens, self.masked, self.seq_steps,
                        self.eos_block, self.counters, self.trace if trace else None, self.ws, stream)
 
+    def capture(self, trace: bool = True) -> "torch.cuda.CUDAGraph":
+        """Record one whole generation (every launch fdl_decode enqueues) in a
+        HIP graph; replaying it reruns the generation from the prompt.  The
+        loop reinitializes all of its state on the device, and none of its
+        launches is a memset, so replays need no host-side reset."""
+        side = torch.cuda.Stream(device=self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            self.run(trace=trace)                     # warm-up outside the capture
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(trace=trace)
+        return graph
+
     def results(self) -> dict:
         """Host copies of the outputs; the trace as a list of per-step dicts."""
         c = self.counters.cpu().numpy()

@@ -204,3 +204,34 @@ def test_decode_workload_shapes_bf16(name, max_blocks):
     ref = _oracle(run)
     res = _compare(run, got, ref)
     print(f"steps {got['steps']} excluded {res['excluded']} forked {res['forked']}", flush=True)
+
+
+def test_decode_graph_replay():
+    """The whole generation captured in a HIP graph: every replay, with eager
+    work of another run and synchronizations in between, equals the eager run."""
+    _need_gpu()
+    print("decode graph replay", flush=True)
+    cfg = _tiny()
+    run = DecodeRunner(cfg, seed=8)
+    other = DecodeRunner(cfg, seed=9)
+    run.run()
+    torch.cuda.synchronize()
+    eager = run.results()
+    graph = run.capture()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        other.run()                       # eager work between replays
+        torch.cuda.synchronize()
+        run.tokens.zero_()
+        run.masked.fill_(1)
+        run.counters.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = run.results()
+        for key in ("tokens", "masked", "seq_steps", "eos_block", "length", "k_cache", "v_cache"):
+            np.testing.assert_array_equal(got[key], eager[key], err_msg=f"replay {rep}: {key}")
+        assert (got["steps"], got["blocks_run"]) == (eager["steps"], eager["blocks_run"])
+        for a, b in zip(got["trace"], eager["trace"]):
+            np.testing.assert_array_equal(a["tokens"], b["tokens"])
+            np.testing.assert_array_equal(a["conf"], b["conf"])
