@@ -142,13 +142,21 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
       if (xdst[p] >= 0) Xs[buf][xdst[p]] = xreg[p];
   };
 
+  // Workgroup b walks the K slabs starting at slab (5 b) mod nslab: when the
+  // row stride is a multiple of the HBM channel interleave (H = 4096: 8 KB)
+  // the workgroups in flight would otherwise all read the same low address
+  // bits at the same time and queue on a few channels (measured at H = 4096:
+  // 255 -> 196 us per call; strides 1, 5, 13, 29 all alike).  The sum order
+  // differs per workgroup but is fixed.
   const int nslab = a.H / KSLAB;
-  gload(0);
+  const int rot = int((5u * blockIdx.x) % unsigned(nslab));
+  auto kslab = [&](int sl) { return (sl + rot < nslab ? sl + rot : sl + rot - nslab) * KSLAB; };
+  gload(kslab(0));
   lstore(0);
   __syncthreads();
   for (int sl = 0; sl < nslab; ++sl) {
     const int buf = sl & 1;
-    if (sl + 1 < nslab) gload((sl + 1) * KSLAB);
+    if (sl + 1 < nslab) gload(kslab(sl + 1));
 #pragma unroll
     for (int ks = 0; ks < KSLAB / 32; ++ks) {
       const int c = ks * 4 + grp;
