@@ -452,7 +452,37 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
   // two register stages: tile t + 2 is fetched while tile t is computed
   u32x4 kreg[2][KCH_T];
   u32x4 vreg[2][VU_T][4];
+  // Per-thread source offsets of the K and V chunks within a tile; a tile that
+  // lies wholly inside the cache (no block keys, no key past the split) takes
+  // them with a scalar offset, the rest go through the per-key selection.
+  int koff[KCH_T], voff[VU_T][4];
+#pragma unroll
+  for (int c = 0; c < KCH_T; ++c) {
+    const int ch = tid + c * NT;
+    koff[c] = (ch / CPR) * DH + (ch % CPR) * EPC;
+  }
+#pragma unroll
+  for (int u = 0; u < VU_T; ++u) {
+    const int un = tid + u * NT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) voff[u][e] = ((un % (TK / 4)) * 4 + e) * DH + (un / (TK / 4)) * EPC;
+  }
   auto load_tile = [&](int rs, int key0) {
+    const bool fast = key0 + TK <= k_end && (key0 + TK <= lp || key0 >= lp + a.D);
+    if (fast) {
+      const T* kt = kc + size_t(key0) * DH;
+      const T* vt = vc + size_t(key0) * DH;
+#pragma unroll
+      for (int c = 0; c < KCH_T; ++c)
+        if (KCH % NT == 0 || tid + c * NT < KCH) kreg[rs][c] = ld16(kt + koff[c]);
+#pragma unroll
+      for (int u = 0; u < VU_T; ++u)
+        if (VU % NT == 0 || tid + u * NT < VU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vreg[rs][u][e] = ld16(vt + voff[u][e]);
+        }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < KCH_T; ++c) {
       const int ch = tid + c * NT;
@@ -534,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][kt][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      mx = xor32_max(mx) * c;
       // lazy rescale: keep the running reference unless the new maximum
       // exceeds it by more than 8 (log2 units); p then stays below 2^8
       if (__builtin_amdgcn_ballot_w64(mx > m[j] + 8.f) != 0) {
@@ -555,7 +585,7 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
           s[j][kt][v] = p;
           rs += p;
         }
-      rs += __shfl_xor(rs, 32, 64);
+      rs = xor32_sum(rs);
       l[j] += rs;
     }
     // O^T += V^T P^T over 16-key chunks (kt, q)

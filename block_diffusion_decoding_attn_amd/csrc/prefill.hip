@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    mx = xor32_max(mx) * c;
     // lazy rescale (see the block attention kernel); a fully masked tile
     // (mx = -inf) leaves the state untouched
     if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s[kt][v] = p;
         rs += p;
       }
-    rs += __shfl_xor(rs, 32, 64);
+    rs = xor32_sum(rs);
     l += rs;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
