@@ -12,13 +12,15 @@
 //     heads x S query rows of a KV head live in the workgroup, so every K/V
 //     byte of a split is read from HBM exactly once per step.
 //   * K/V tiles of 64 keys are staged through LDS by 16-byte coalesced loads,
-//     prefetched into registers one tile ahead of the MFMA work.  V is written
-//     to LDS transposed so that the P.V product reads contiguous keys.
-//   * S^T = K Q^T and O^T = V^T P^T run on MFMA (16x16x32 bf16, or 16x16x4 f32
-//     for f32 data).  In this orientation the score accumulator of a lane is
-//     exactly the P operand of the next MFMA (same query column, the same 8
-//     keys), and the per-query softmax statistics sit in the lane that owns
-//     that query column, so the online-softmax rescale needs no shuffles.
+//     prefetched into registers ahead of the MFMA work (two tiles ahead for
+//     bf16, one for f32).  V is written to LDS transposed so that the P.V
+//     product reads contiguous keys.
+//   * S^T = K Q^T and O^T = V^T P^T run on MFMA (32x32x16 bf16, or 16x16x4
+//     f32 for f32 data).  In this orientation the score accumulator of a lane
+//     is exactly the P operand of the next MFMA (same query column, the same
+//     keys under a fixed permutation), and the per-query softmax statistics
+//     sit in the lane that owns that query column, so the online-softmax
+//     rescale needs no shuffles.
 //   * Online softmax in fp32 with exp2 and the log2(e)/sqrt(d) scale folded
 //     into the scores.  Splits write (m, l, unnormalized O) partials that a
 //     second kernel merges in a fixed order (deterministic).

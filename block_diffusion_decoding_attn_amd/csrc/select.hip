@@ -12,9 +12,11 @@
 // gfx950 design: the logits are an HBM stream of 4 M V bytes.  Kernel 1 splits
 // every row into chunks so that thousands of workgroups stream it with 16-byte
 // loads, each reducing its chunk to (max, lowest argmax, sum exp(l - max)).
-// Kernel 2 (one workgroup per sequence) merges the chunk partials of each row
-// in chunk order -- the result does not depend on scheduling -- and applies
-// the selection rule, then writes the commit set and updates tokens/masked.
+// (The fused LM head writes the same partials from its epilogue instead.)
+// Kernel 2 (one workgroup per row) merges a row's partials in a fixed order --
+// the result does not depend on scheduling -- and the workgroup that finishes
+// a sequence's last row applies the selection rule, then writes the commit set
+// and updates tokens/masked.
 #include <climits>
 
 #include "common.h"

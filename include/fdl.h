@@ -175,7 +175,9 @@ int fdl_prefill_attn(const fdl_dims* dims, int32_t q_start, int32_t n_q, int32_t
 int fdl_lm_head(const fdl_dims* dims, int32_t rows, const void* x, const void* w,
                 float* logits, void* stream);
 
-/* Bytes of device workspace fdl_conf_select needs (0 for invalid arguments). */
+/* Bytes of device workspace fdl_conf_select needs: chunk partials of every
+ * row and one row counter per sequence (0 for invalid arguments).  Scratch of
+ * one call: calls that overlap on it race. */
 size_t fdl_conf_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq);
 
 /* Confidence select (Algorithm 2 / fixed count / Algorithm 3) with the
@@ -199,7 +201,9 @@ int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* log
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fdl_lm_head_select needs: 16 bytes per (row,
- * 128-row vocabulary tile).  0 for invalid arguments. */
+ * 128-row vocabulary tile) of select partials, then one 4-byte row counter
+ * per sequence (rounded up to 16 bytes).  0 for invalid arguments.  The
+ * workspace is scratch of one call: calls that overlap on it race. */
 size_t fdl_lm_head_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq);
 
 /* LM head fused with the confidence select: the same results as fdl_lm_head
