@@ -260,11 +260,12 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
 // tiled (M > 64): workgroup tile 256 (vocab) x 256 (rows), 8 waves in a 2 x 4
 // grid of 128 x 64 wave tiles (4 x 2 MFMA 32x32x16 tiles each).  K is consumed
 // in 32-wide slabs that travel HBM -> LDS by global_load_lds_dwordx4 (no
-// register staging, so the loads can run TB_NST - 1 slabs ahead of the MFMA
-// work at one workgroup per CU) through a TB_NST-stage ring.  A slab row is
-// 64 bytes = 4 chunks of 16; chunk c of row r sits at chunk c ^ ((r >> 2) & 3)
-// so that the 32-row fragment reads of a wave are free of bank conflicts.
-constexpr int TB_V = 256, TB_M = 256, TB_K = 32, TB_NST = 4, TB_NWV = 2, TB_NWM = 4;
+// register staging) through a TB_NST-stage ring, three slabs ahead of the
+// MFMA work.  A slab row is 64 bytes = 4 chunks of 16; chunk c of row r sits
+// at chunk c ^ ((r >> 2) & 3) so that the 32-row fragment reads of a wave are
+// free of bank conflicts.  Fragment reads are software-pipelined: the eight
+// MFMAs of one 16-wide k-step run while the next k-step's fragments are read.
+constexpr int TB_V = 256, TB_M = 256, TB_K = 32, TB_NST = 5, TB_NWV = 2, TB_NWM = 4;  // 5 x 32 KB: all of LDS
 constexpr int TB_ROWB = TB_K * 2;                          // bytes per row per stage
 constexpr int TB_ABYTES = TB_V * TB_ROWB, TB_STB = (TB_V + TB_M) * TB_ROWB;
 constexpr int TB_NT = TB_NWV * TB_NWM * 64;
@@ -279,6 +280,27 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((((N >> 4) & 3) << 14) | (0xF << 8) | (7 << 4) | (N & 15));
+}
+
+// (max, sum of exp(x - max), lowest argmax) of the 16 values a lane holds of
+// one 32x32 accumulator tile: value e is vocabulary row vb + 8(e/4) + e%4.
+// Rows at or past V do not count.
+__device__ __forceinline__ Red tile_red(const f32x16 t, int vb, int V) {
+  float x[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x[e] = vb + (e / 4) * 8 + (e % 4) < V ? t[e] : -INFINITY;
+  float mt = x[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
+  if (mt == -INFINITY) return red_empty();
+  int it = 0;
+#pragma unroll
+  for (int e = 15; e >= 0; --e)
+    if (x[e] == mt) it = vb + (e / 4) * 8 + (e % 4);
+  float st = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) st += exp2f((x[e] - mt) * kLog2e);
+  return Red{mt, st, it};
 }
 
 __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
@@ -333,49 +355,69 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
 
   const int nk = a.H / TB_K;
 #pragma unroll
-  for (int s = 0; s < TB_NST - 1; ++s)
+  for (int s = 0; s < TB_NST - 2; ++s)
     if (s < nk) issue(s);
-  for (int t = 0; t < nk; ++t) {
-    // this wave's loads of slab t have landed once at most the later slabs'
-    // loads are in flight; after the barrier every wave's have
-    if (t + TB_NST - 2 < nk) wait_vmcnt<(TB_NST - 2) * TB_IPW>();
-    else wait_vmcnt<0>();
-    // a bare barrier: __syncthreads() would also wait for the loads still in flight
-    __builtin_amdgcn_s_barrier();
-    // the buffer refilled here held slab t - 1, which every wave has finished
-    if (t + TB_NST - 1 < nk) issue(t + TB_NST - 1);
-    const char* sb = smem + (t % TB_NST) * TB_STB;
+  // the fragments of one 16-wide k-step of a slab
+  auto frag = [&](int slab, int ks, u32x4* af, u32x4* bf) __attribute__((always_inline)) {
+    const char* sb = smem + (slab % TB_NST) * TB_STB;
     const bf16_t* As = reinterpret_cast<const bf16_t*>(sb);
     const bf16_t* Bs = reinterpret_cast<const bf16_t*>(sb + TB_ABYTES);
-    u32x4 af[2][TB_TV], bf[2][TB_TM];
-    auto frag = [&](int ks, int p) {
-      const int c = 2 * ks + half;
+    const int c = 2 * ks + half;
 #pragma unroll
-      for (int i = 0; i < TB_TV; ++i) {
-        const int r = wv0 + i * 32 + l32;
-        af[p][i] = *reinterpret_cast<const u32x4*>(As + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
-      }
+    for (int i = 0; i < TB_TV; ++i) {
+      const int r = wv0 + i * 32 + l32;
+      af[i] = *reinterpret_cast<const u32x4*>(As + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
+    }
 #pragma unroll
-      for (int j = 0; j < TB_TM; ++j) {
-        const int r = wm0 + j * 32 + l32;
-        bf[p][j] = *reinterpret_cast<const u32x4*>(Bs + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
-      }
-    };
-    auto mma = [&](int p) {
+    for (int j = 0; j < TB_TM; ++j) {
+      const int r = wm0 + j * 32 + l32;
+      bf[j] = *reinterpret_cast<const u32x4*>(Bs + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
+    }
+  };
+  auto mma = [&](const u32x4* af, const u32x4* bf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < TB_TV; ++i)
+    for (int i = 0; i < TB_TV; ++i)
 #pragma unroll
-        for (int j = 0; j < TB_TM; ++j) acc[i][j] = mfma32x32x16_bf16(af[p][i], bf[p][j], acc[i][j]);
-    };
-    // both k-steps' fragments are read before the MFMAs of the first start
-    frag(0, 0);
+      for (int j = 0; j < TB_TM; ++j) acc[i][j] = mfma32x32x16_bf16(af[i], bf[j], acc[i][j]);
+  };
+  // slab t has landed once this wave's own loads of it are done (at most the
+  // two later slabs' loads in flight) and, after the barrier, every wave's.
+  // A bare barrier: __syncthreads() would also wait for the later loads.
+  auto arrive = [&](int t) __attribute__((always_inline)) {
+    if (t + TB_NST - 3 < nk) wait_vmcnt<(TB_NST - 3) * TB_IPW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  // Each group of eight MFMAs runs while the next k-step's fragments are
+  // read.  An explicit LDS wait right after the group (whose MFMAs take
+  // hundreds of cycles to issue) completes those reads, so the compiler puts
+  // no wait of its own in front of the next group; every loop iteration has
+  // the same shape (the last slab is peeled) so its wait counts stay exact.
+  constexpr int LGKM0 = 0xC07F;  // s_waitcnt lgkmcnt(0), the other counters untouched
+  u32x4 a0[TB_TV], b0[TB_TM], a1[TB_TV], b1[TB_TM];
+  arrive(0);
+  if (TB_NST - 2 < nk) issue(TB_NST - 2);
+  frag(0, 0, a0, b0);
+  __builtin_amdgcn_s_waitcnt(LGKM0);
+  for (int t = 0; t + 1 < nk; ++t) {
+    frag(t, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    frag(1, 1);
+    mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(0);
+    __builtin_amdgcn_s_waitcnt(LGKM0);
+    arrive(t + 1);
+    frag(t + 1, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(1);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(LGKM0);
+    // the buffer refilled here held slab t - 1, whose fragments every wave
+    // read and waited for before the barrier above
+    if (t + TB_NST - 1 < nk) issue(t + TB_NST - 1);
   }
+  frag(nk - 1, 1, a1, b1);
+  mma(a0, b0);
+  mma(a1, b1);
 
   // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile; a
   // wave's 128 vocabulary rows are exactly one tile of the select partials
@@ -384,12 +426,10 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
     for (int j = 0; j < TB_TM; ++j) {
       Red r = red_empty();
 #pragma unroll
-      for (int i = 0; i < TB_TV; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int v = v0 + wv0 + i * 32 + (e / 4) * 8 + half * 4 + (e % 4);
-          if (v < a.V) push(r, acc[i][j][e], v);
-        }
+      for (int i = 0; i < TB_TV; ++i) {
+        __builtin_amdgcn_sched_barrier(0);  // one accumulator tile at a time
+        r = combine(r, tile_red(acc[i][j], v0 + wv0 + i * 32 + half * 4, a.V));
+      }
       r = combine(r, shfl_xor_red(r, 32));
       const int m = m0 + wm0 + j * 32 + l32;
       if (half == 0 && m < a.M) a.part[size_t(m) * a.nc + (v0 + wv0) / 128] = pack_red(r);

@@ -61,6 +61,13 @@ def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
     (dict(dtype="f32", n_q_heads=4, n_kv_heads=2, head_dim=64, sub_block=32, prompt_len=70, gen_len=64), 1, [3, 102]),
     (dict(prompt_len=0, gen_len=32, sub_block=32, n_q_heads=2, n_kv_heads=1), 0, None),      # only the block
     (dict(batch=3, prompt_len=2000, gen_len=64), 1, [2000, 5, 2032]),   # many splits, some empty
+    # more than 128 rows per KV head: the two-group (ping-pong) kernel
+    (dict(n_q_heads=8, n_kv_heads=1, sub_block=32, prompt_len=0, gen_len=32), 0, None),      # 256 rows, one tile
+    (dict(n_q_heads=28, n_kv_heads=4, sub_block=32, prompt_len=64, gen_len=64), 0, None),    # two tiles, one split
+    (dict(n_q_heads=16, n_kv_heads=2, sub_block=32, prompt_len=200, gen_len=96), 2, [0, 203]),
+    (dict(n_q_heads=20, n_kv_heads=4, sub_block=32, batch=1, prompt_len=1000, gen_len=64), 1, None),  # 160 rows
+    (dict(n_q_heads=28, n_kv_heads=4, sub_block=32, batch=8, prompt_len=1440, gen_len=96), 2, None),  # 3-tile splits
+    (dict(attn_mode=synth.DUAL_CACHE, n_q_heads=8, n_kv_heads=1, sub_block=32), 1, None),    # DualCache, 256 rows
 ])
 def test_block_attn_parity(kw, block_idx, prefix):
     cfg = _cfg(**kw)
