@@ -181,7 +181,7 @@ int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* log
 
 size_t fdl_lm_head_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq) {
   if (check_dims(dims) != FDL_OK || rows_per_seq < 1 || rows_per_seq > 256) return 0;
-  return partials_workspace_bytes(*dims, rows_per_seq, lm_head_tiles(*dims));
+  return partials_workspace_bytes(*dims, rows_per_seq, lm_head_tiles(*dims, dims->batch * rows_per_seq));
 }
 
 int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x, const void* w, float* logits,
@@ -197,7 +197,7 @@ int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x
   const int rows = d.batch * rows_per_seq;
   rc = check_lm_head_args(d, rows, x, w);
   if (rc != FDL_OK) return rc;
-  const int nc = lm_head_tiles(d);
+  const int nc = lm_head_tiles(d, rows);
   if (!workspace || workspace_bytes < partials_workspace_bytes(d, rows_per_seq, nc)) return FDL_E_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   rc = lm_head_launch(d, rows, x, w, logits, workspace, st);

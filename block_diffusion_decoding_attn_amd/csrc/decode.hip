@@ -329,7 +329,7 @@ static DecLayout decode_layout(const fdl_dims& d) {
   L.vb = take(size_t(d.batch) * d.n_kv_heads * d.block * d.head_dim * es);
   L.o = take(rows * d.hidden * es);
   L.x = take(rows * d.hidden * es);
-  L.part = take(partials_workspace_bytes(d, d.sub_block, lm_head_tiles(d)));
+  L.part = take(partials_workspace_bytes(d, d.sub_block, lm_head_tiles(d, d.batch * d.sub_block)));
   L.attn = take(attn_workspace_bytes(d));
   L.tok = take(rows * sizeof(int32_t));
   L.conf = take(rows * sizeof(float));
@@ -373,7 +373,7 @@ int decode_launch(const fdl_dims& d, const fdl_decode_args& g, void* ws, hipStre
   const int nblocks = g.max_blocks > 0 ? g.max_blocks : L / D;
   const int slots = decode_slots_per_sub(d, g.mode, g.k);
   const bool bf = d.dtype == FDL_BF16;
-  const int nc = lm_head_tiles(d);
+  const int nc = lm_head_tiles(d, d.batch * d.sub_block);
 
   DecArgs a;
   a.tokens = g.tokens; a.masked = g.masked; a.len = g.len; a.seq_steps = g.seq_steps; a.eos_block = g.eos_block;

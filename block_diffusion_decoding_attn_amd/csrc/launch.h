@@ -15,7 +15,7 @@ int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc,
                 size_t ws_bytes, hipStream_t st, const int32_t* gate = nullptr);
 int prefill_launch(const fdl_dims& d, int q_start, int n_q, int n_keys, int causal, const void* q, const void* k,
                    const void* v, void* out, float* lse, hipStream_t st);
-int lm_head_tiles(const fdl_dims& d);
+int lm_head_tiles(const fdl_dims& d, int rows);
 // part: null, or a partials workspace laid out for rows / d.batch rows per
 // sequence (partials_workspace_bytes), whose counters the launch zeroes
 int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,

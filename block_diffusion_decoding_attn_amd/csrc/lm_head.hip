@@ -27,6 +27,7 @@ struct LmArgs {
   const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
   int32_t* cnt;         // select row counters to zero (with part), or null
   int ncnt;
+  int span;             // skinny bf16: vocabulary rows per workgroup (at most 128)
 };
 
 // Workgroup 0 zeroes the select's per-sequence row counters for the
@@ -38,12 +39,13 @@ __device__ __forceinline__ void zero_counters(const LmArgs& a) {
 
 // Fused-select epilogue, shared by the skinny kernels: lane holds
 // acc[t][n][e] = logit of vocabulary row vbase + 16t + 4grp + e for column
-// m = 16n + l16.  Reduce each column over the lane's rows (increasing index),
-// then over the 4 lane groups, then over the workgroup's waves through LDS,
-// and write one partial per (row, 128-row vocabulary tile).
+// m = 16n + l16; rows at or past vend do not count.  Reduce each column over
+// the lane's rows (increasing index), then over the 4 lane groups, then over
+// the workgroup's waves through LDS, and write the workgroup's partial for
+// each row (partial index tile = the workgroup's vocabulary range).
 template <int RT, int NTM, int NWAVES>
-__device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (&acc)[RT][NTM], int vbase, int wave,
-                                                  int l16, int grp, int tile, f32x4 (*red)[NTM * 16]) {
+__device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (&acc)[RT][NTM], int vbase, int vend,
+                                                  int wave, int l16, int grp, int tile, f32x4 (*red)[NTM * 16]) {
 #pragma unroll
   for (int n = 0; n < NTM; ++n) {
     Red r = red_empty();
@@ -52,7 +54,7 @@ __device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = vbase + t * 16 + grp * 4 + e;
-        if (v < a.V) push(r, acc[t][n][e], v);
+        if (v < vend) push(r, acc[t][n][e], v);
       }
     r = combine(r, shfl_xor_red(r, 16));
     r = combine(r, shfl_xor_red(r, 32));
@@ -69,17 +71,27 @@ __device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (
 }
 
 // ---------------------------------------------------------------------------
-// skinny: a workgroup of WPB waves owns ROWS vocabulary rows.  K is walked in
-// slabs of KSLAB: the W slab (ROWS x KSLAB) and the X slab (16 NTM x KSLAB)
-// are fetched with 16-byte loads in which 8 consecutive lanes cover one
-// row's 128 contiguous bytes, the next slab is held in registers while the
-// current one is consumed, and both are written XOR-swizzled into a
-// double-buffered LDS, from which every wave reads its MFMA fragments
-// (A = 16 W rows x 32 k, B = 32 k x 16 X rows).  Staging X in LDS once per
-// workgroup keeps the X re-reads off the L2 path (measured: 5.8 TB/s against
-// 4.5 TB/s when every wave fetched its own X fragments).
-template <int NTM, int ROWS, int KSLAB, int WPB>
-__global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
+// skinny: a workgroup of WPB waves owns a contiguous range of a.span <= ROWS
+// vocabulary rows, [b span, (b + 1) span) for workgroup b.  K is walked
+// in slabs of KSLAB: the W slab (ROWS x KSLAB) and the X slab (16 NTM x
+// KSLAB) are fetched with 16-byte loads in which 8 consecutive lanes cover one
+// row's 128 contiguous bytes (rows past the range are not fetched), the next
+// slab is held in registers while the current one is consumed, and both are
+// written XOR-swizzled into LDS, from which every wave reads its MFMA
+// fragments (A = 16 W rows x 32 k, B = 32 k x 16 X rows).  Staging X in LDS
+// once per workgroup keeps the X re-reads off the L2 path (measured: 5.8 TB/s
+// against 4.5 TB/s when every wave fetched its own X fragments).
+//
+// ONEBUF (up to 32 rows): one LDS buffer (22.5 KB, two barriers per slab) and
+// at most 96 VGPRs, so that five workgroups fit on a CU and the launch can
+// hold up to 1280 workgroups resident at once on MI355X's 256 CUs; the span
+// is then V / 1280 rounded up (119 rows for 152064), so every workgroup
+// streams the same share of W from the first cycle to the last.  With 128-row tiles (1188 for a 152064-row vocabulary) at three per
+// CU the launch ran in two rounds, the second one 55% full (measured per
+// workgroup: 7.3 TB/s while all slots were busy, 5.5-6 TB/s in the second
+// round).  Otherwise (33-64 rows) a double-buffered LDS with one barrier.
+template <int NTM, int ROWS, int KSLAB, int WPB, bool ONEBUF>
+__device__ __forceinline__ void skinny_bf16_body(const LmArgs& a) {
   if (gate_closed(a.gate)) return;
   zero_counters(a);
   constexpr int NT = WPB * 64;
@@ -90,24 +102,26 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
   constexpr int XPER = (XCH + NT - 1) / NT;
   constexpr int RPW = ROWS / WPB;            // rows per wave
   constexpr int RT = RPW / 16;
+  constexpr int NBUF = ONEBUF ? 1 : 2;
   static_assert(WCH % NT == 0 && RPW % 16 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) u32x4 Ws[2][WCH];
-  __shared__ __attribute__((aligned(16))) u32x4 Xs[2][XCH];
+  __shared__ __attribute__((aligned(16))) u32x4 Ws[NBUF][WCH];
+  __shared__ __attribute__((aligned(16))) u32x4 Xs[NBUF][XCH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int v0 = blockIdx.x * ROWS;
+  const int v0 = min(a.V, int(blockIdx.x) * a.span), v1 = min(a.V, v0 + a.span);
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
 
-  // per-thread staging sources (rows clamped at the vocabulary tail, X rows past M read as zero)
+  // per-thread staging sources (W rows past the range and X rows past M read as zero)
   const bf16_t* wsrc[WPER];
   int wdst[WPER];
+  bool wok[WPER];
 #pragma unroll
   for (int p = 0; p < WPER; ++p) {
     const int ch = tid + p * NT, row = ch / CPR, c = ch % CPR;
-    const int vr = v0 + row < a.V ? v0 + row : a.V - 1;
-    wsrc[p] = W + size_t(vr) * a.H + c * 8;
+    wok[p] = v0 + row < v1;
+    wsrc[p] = W + size_t(wok[p] ? v0 + row : v0) * a.H + c * 8;
     wdst[p] = row * CPR + (c ^ (row % CPR));
   }
   const bf16_t* xsrc[XPER];
@@ -130,7 +144,7 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
   u32x4 wreg[WPER], xreg[XPER];
   auto gload = [&](int k) {
 #pragma unroll
-    for (int p = 0; p < WPER; ++p) wreg[p] = ld16_stream(wsrc[p] + k);
+    for (int p = 0; p < WPER; ++p) wreg[p] = wok[p] ? ld16_stream(wsrc[p] + k) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int p = 0; p < XPER; ++p) xreg[p] = xok[p] ? ld16(xsrc[p] + k) : u32x4{0, 0, 0, 0};
   };
@@ -141,22 +155,7 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
     for (int p = 0; p < XPER; ++p)
       if (xdst[p] >= 0) Xs[buf][xdst[p]] = xreg[p];
   };
-
-  // Workgroup b walks the K slabs starting at slab (5 b) mod nslab: when the
-  // row stride is a multiple of the HBM channel interleave (H = 4096: 8 KB)
-  // the workgroups in flight would otherwise all read the same low address
-  // bits at the same time and queue on a few channels (measured at H = 4096:
-  // 255 -> 196 us per call; strides 1, 5, 13, 29 all alike).  The sum order
-  // differs per workgroup but is fixed.
-  const int nslab = a.H / KSLAB;
-  const int rot = int((5u * blockIdx.x) % unsigned(nslab));
-  auto kslab = [&](int sl) { return (sl + rot < nslab ? sl + rot : sl + rot - nslab) * KSLAB; };
-  gload(kslab(0));
-  lstore(0);
-  __syncthreads();
-  for (int sl = 0; sl < nslab; ++sl) {
-    const int buf = sl & 1;
-    if (sl + 1 < nslab) gload(kslab(sl + 1));
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < KSLAB / 32; ++ks) {
       const int c = ks * 4 + grp;
@@ -174,14 +173,44 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
         for (int n = 0; n < NTM; ++n) acc[t][n] = mfma16x16x32_bf16(wf, xb[n], acc[t][n]);
       }
     }
-    if (sl + 1 < nslab) lstore(buf ^ 1);
+  };
+
+  // Workgroup b walks the K slabs starting at slab (5 b) mod nslab: when the
+  // row stride is a multiple of the HBM channel interleave (H = 4096: 8 KB)
+  // the workgroups in flight would otherwise all read the same low address
+  // bits at the same time and queue on a few channels (measured at H = 4096:
+  // 255 -> 196 us per call; strides 1, 5, 13, 29 all alike).  The sum order
+  // differs per workgroup but is fixed.
+  const int nslab = a.H / KSLAB;
+  const int rot = int((5u * blockIdx.x) % unsigned(nslab));
+  auto kslab = [&](int sl) { return (sl + rot < nslab ? sl + rot : sl + rot - nslab) * KSLAB; };
+  gload(kslab(0));
+  if (ONEBUF) {
+    // the next slab waits in registers and is stored once every wave has
+    // finished reading the current one
+    for (int sl = 0; sl < nslab; ++sl) {
+      if (sl > 0) __syncthreads();
+      lstore(0);
+      __syncthreads();
+      if (sl + 1 < nslab) gload(kslab(sl + 1));
+      compute(0);
+    }
+  } else {
+    lstore(0);
     __syncthreads();
+    for (int sl = 0; sl < nslab; ++sl) {
+      const int buf = sl & 1;
+      if (sl + 1 < nslab) gload(kslab(sl + 1));
+      compute(buf);
+      if (sl + 1 < nslab) lstore(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   // lane holds C[vocab v0 + wave*RPW + 16t + 4grp + e][m = 16n + l16]
   if (a.part) {
     __shared__ f32x4 red[WPB][NTM * 16];
-    epilogue_partials<RT, NTM, WPB>(a, acc, v0 + wave * RPW, wave, l16, grp, blockIdx.x, red);
+    epilogue_partials<RT, NTM, WPB>(a, acc, v0 + wave * RPW, v1, wave, l16, grp, blockIdx.x, red);
   }
   if (!a.out) return;
 #pragma unroll
@@ -192,15 +221,29 @@ __global__ __launch_bounds__(WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int v = v0 + wave * RPW + t * 16 + grp * 4;
-      if (v + 3 < a.V && (a.V & 3) == 0) {
+      if (v + 3 < v1 && ((v | a.V) & 3) == 0) {
         *reinterpret_cast<f32x4*>(orow + v) = acc[t][n];
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (v + e < a.V) orow[v + e] = acc[t][n][e];
+          if (v + e < v1) orow[v + e] = acc[t][n][e];
       }
     }
   }
+}
+
+constexpr int SK_ROWS = 128, SK_KSLAB = 64, SK_WPB = 4;
+constexpr int SK_RESIDENT = 1280;  // workgroups resident at once: 5 per CU x 256 CUs
+
+template <int NTM>
+__global__ __launch_bounds__(SK_WPB * 64) __attribute__((amdgpu_waves_per_eu(5, 5))) void lm_head_skinny_bf16_one(
+    LmArgs a) {
+  skinny_bf16_body<NTM, SK_ROWS, SK_KSLAB, SK_WPB, true>(a);
+}
+
+template <int NTM>
+__global__ __launch_bounds__(SK_WPB * 64) void lm_head_skinny_bf16(LmArgs a) {
+  skinny_bf16_body<NTM, SK_ROWS, SK_KSLAB, SK_WPB, false>(a);
 }
 
 // f32 data (the small fp32 workload): same wave decomposition on the
@@ -239,7 +282,7 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
   }
   if (a.part) {  // a workgroup covers 4 waves x RT*16 = 128 vocabulary rows when RT = 2
     __shared__ f32x4 red[4][NTM * 16];
-    epilogue_partials<RT, NTM, 4>(a, acc, v0, wave, l16, grp, blockIdx.x, red);
+    epilogue_partials<RT, NTM, 4>(a, acc, v0, a.V, wave, l16, grp, blockIdx.x, red);
   }
   if (!a.out || v0 >= a.V) return;
 #pragma unroll
@@ -461,11 +504,25 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 
+// Vocabulary rows per workgroup of the bf16 skinny LM head: up to 32 rows
+// with a large vocabulary, V / SK_RESIDENT rounded up (all workgroups
+// resident at once), else 128.
+static int skinny_span(int V, int rows) {
+  if (rows <= 32 && V >= 64 * SK_RESIDENT && V <= SK_ROWS * SK_RESIDENT) return (V + SK_RESIDENT - 1) / SK_RESIDENT;
+  return SK_ROWS;
+}
+static int skinny_workgroups(int V, int rows) {
+  const int span = skinny_span(V, rows);
+  return (V + span - 1) / span;
+}
+
 template <int NTM>
-static void launch_skinny_bf16(const LmArgs& a, hipStream_t st) {
-  constexpr int ROWS = 128, KSLAB = 64, WPB = 4;
-  hipLaunchKernelGGL((lm_head_skinny_bf16<NTM, ROWS, KSLAB, WPB>), dim3((a.V + ROWS - 1) / ROWS), dim3(WPB * 64), 0,
-                     st, a);
+static void launch_skinny_bf16(const LmArgs& args, hipStream_t st) {
+  LmArgs a = args;
+  a.span = skinny_span(a.V, a.M);
+  const dim3 grid(skinny_workgroups(a.V, a.M));
+  if constexpr (NTM <= 2) hipLaunchKernelGGL(lm_head_skinny_bf16_one<NTM>, grid, dim3(SK_WPB * 64), 0, st, a);
+  else hipLaunchKernelGGL(lm_head_skinny_bf16<NTM>, grid, dim3(SK_WPB * 64), 0, st, a);
 }
 
 template <int NTM>
@@ -475,12 +532,15 @@ static void launch_skinny_f32(const LmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((lm_head_skinny_f32<NTM, RT>), dim3((waves + 3) / 4), dim3(256), 0, st, a);
 }
 
-int lm_head_tiles(const fdl_dims& d) { return (d.vocab + 127) / 128; }
+int lm_head_tiles(const fdl_dims& d, int rows) {
+  if (d.dtype == FDL_BF16 && rows <= 64) return skinny_workgroups(d.vocab, rows);
+  return (d.vocab + 127) / 128;  // tiled kernel and f32: one partial per 128-row vocabulary tile
+}
 
 int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,
                    hipStream_t st, const int32_t* gate) {
-  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d), gate,
-           nullptr, 0};
+  LmArgs a{x, w, logits, reinterpret_cast<f32x4*>(part), rows, d.hidden, d.vocab, lm_head_tiles(d, rows), gate,
+           nullptr, 0, SK_ROWS};
   if (part) {
     a.cnt = partials_counters(part, d, rows / d.batch, a.nc);
     a.ncnt = d.batch;

@@ -98,6 +98,7 @@ def test_block_attn_deterministic():
     (1, 512, 1000, "bf16"), (7, 512, 1003, "bf16"), (16, 256, 4096, "bf16"), (32, 3584, 2048, "bf16"),
     (33, 512, 1000, "bf16"), (64, 1024, 1000, "bf16"), (100, 512, 1000, "bf16"), (300, 512, 1003, "bf16"),
     (32, 256, 512, "f32"), (5, 260, 77, "f32"), (64, 256, 512, "f32"),
+    (16, 256, 100003, "bf16"), (32, 128, 152064, "bf16"),     # 79 / 119 vocabulary rows per workgroup
 ])
 def test_lm_head_parity(M, H, V, dtype):
     dev = _dev()
@@ -239,6 +240,10 @@ def test_kv_append_bitwise(kw, lens, n_new):
     (5, 32, 256, 1000, "bf16", O.SELECT_THRESHOLD),     # M = 160: tiled kernel
     (1, 32, 256, 512, "f32", O.SELECT_THRESHOLD),
     (2, 8, 260, 77, "f32", O.SELECT_TOPK),
+    # large vocabularies, up to 32 rows: all workgroups resident, 64-128 rows each
+    (2, 8, 256, 100003, "bf16", O.SELECT_THRESHOLD),    # 79 rows per workgroup, ragged last
+    (4, 8, 128, 152064, "bf16", O.SELECT_TOPK),         # the Qwen2.5 vocabulary: 119 rows each
+    (1, 32, 192, 126464, "bf16", O.SELECT_FACTOR),      # the LLaDA vocabulary: 99 rows each
 ])
 def test_lm_head_select_parity(B, R, H, V, dtype, mode):
     """Fused LM head + select against the oracle (logits in fp64, select on
