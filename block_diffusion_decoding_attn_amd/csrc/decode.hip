@@ -55,7 +55,9 @@ struct Chunk<float> {
     const f32x4 x = *reinterpret_cast<const f32x4*>(p);
     v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
   }
-  __device__ static void store(float* p, const float* v) { *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]}; }
+  __device__ static void store(float* p, const float* v) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
 };
 template <>
 struct Chunk<bf16_t> {

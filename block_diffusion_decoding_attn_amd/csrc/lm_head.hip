@@ -22,7 +22,7 @@ struct LmArgs {
   const void* x;
   const void* w;
   float* out;    // [M][V] logits, or null (fused select: only partials)
-  f32x4* part;   // [M][nc] confidence partials per 128-row vocabulary tile, or null
+  f32x4* part;   // [M][nc] confidence partials, one per workgroup vocabulary span, or null
   int M, H, V, nc;
   const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
   int32_t* cnt;         // select row counters to zero (with part), or null
@@ -86,10 +86,11 @@ __device__ __forceinline__ void epilogue_partials(const LmArgs& a, const f32x4 (
 // at most 96 VGPRs, so that five workgroups fit on a CU and the launch can
 // hold up to 1280 workgroups resident at once on MI355X's 256 CUs; the span
 // is then V / 1280 rounded up (119 rows for 152064), so every workgroup
-// streams the same share of W from the first cycle to the last.  With 128-row tiles (1188 for a 152064-row vocabulary) at three per
-// CU the launch ran in two rounds, the second one 55% full (measured per
-// workgroup: 7.3 TB/s while all slots were busy, 5.5-6 TB/s in the second
-// round).  Otherwise (33-64 rows) a double-buffered LDS with one barrier.
+// streams the same share of W from its first cycle.  With 128-row tiles
+// (1188 for a 152064-row vocabulary) at three per CU the launch ran in two
+// rounds, the second one 55% full (measured per workgroup: 7.3 TB/s while
+// all slots were busy, 5.5-6 TB/s in the second round).  Otherwise (33-64
+// rows) a double-buffered LDS with one barrier.
 template <int NTM, int ROWS, int KSLAB, int WPB, bool ONEBUF>
 __device__ __forceinline__ void skinny_bf16_body(const LmArgs& a) {
   if (gate_closed(a.gate)) return;

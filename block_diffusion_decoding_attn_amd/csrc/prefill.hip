@@ -34,7 +34,8 @@ struct PrefillArgs {
 constexpr int PF_TK = 64;
 
 template <int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_bf16_kernel(
+    PrefillArgs a) {
   typedef bf16_t T;
   constexpr int NT = 256, TK = PF_TK;
   constexpr int KSTEPS = DH / 16, DT = DH / 32;

@@ -201,14 +201,16 @@ int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* log
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace fdl_lm_head_select needs: 16 bytes per (row,
- * 128-row vocabulary tile) of select partials, then one 4-byte row counter
- * per sequence (rounded up to 16 bytes).  0 for invalid arguments.  The
+ * vocabulary span) of select partials -- a span is the vocabulary range of
+ * one LM-head workgroup: 128 rows, or V / 1280 rounded up for up to 32 rows
+ * and a vocabulary of 81,920 to 163,840 -- then one 4-byte row counter per
+ * sequence (rounded up to 16 bytes).  0 for invalid arguments.  The
  * workspace is scratch of one call: calls that overlap on it race. */
 size_t fdl_lm_head_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq);
 
 /* LM head fused with the confidence select: the same results as fdl_lm_head
  * followed by fdl_conf_select on its logits, but the LM head's epilogue
- * reduces every (row, 128-row vocabulary tile) of logits it computes to the
+ * reduces every (row, vocabulary span) of logits it computes to the
  * select's (max, lowest argmax, sum exp) partial, so the B*R*V f32 logits are
  * neither written nor read back ("Fast-dLLM v2", Level 2: only the argmax and
  * its probability are consumed).  Arguments as in fdl_lm_head (rows =
