@@ -51,9 +51,19 @@ def lm_head_bytes_flops(cfg, fused: bool):
     return byts, flops
 
 
-def pmc_traffic(per_launch_units=1):
+def lm_head_kernel_name(cfg):
+    """The LM-head kernel the library launches for this workload's rows."""
+    if cfg.dtype == "f32":
+        return "lm_head_skinny_f32"
+    if cfg.rows <= 32:
+        return "lm_head_skinny_bf16_one"
+    return "lm_head_skinny_bf16" if cfg.rows <= 64 else "lm_head_tiled_bf16"
+
+
+def pmc_traffic(workload, per_launch_units=1):
     """HBM bytes per launch from the committed rocprofv3 counter summary, scaled
-    by the copy-kernel calibration; None when missing or the kernel changed."""
+    by the copy-kernel calibration; None when missing, taken on another
+    workload, or the kernel source changed since."""
     if not os.path.exists(PROFILE_PMC):
         return None
     kv = {}
@@ -63,7 +73,7 @@ def pmc_traffic(per_launch_units=1):
             kv[k.strip()] = v.strip()
     try:
         sha = hashlib.sha256(open(LM_HEAD_SRC, "rb").read()).hexdigest()
-        if kv.get("source_sha256") != sha:
+        if kv.get("source_sha256") != sha or kv.get("workload") != workload:
             return None
         fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_scale"])
         write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_scale"])
@@ -287,9 +297,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": byts / (lm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = pmc_traffic() if run.fused else None
-    roof["kernel"] = ("fdl_lm_head_select (lm_head_skinny_bf16 with the select epilogue + select_finalize_kernel)"
-                      if run.fused else "fdl_lm_head (lm_head_skinny_bf16)")
+    roof["traffic"] = pmc_traffic(cfg.name) if run.fused else None
+    kname = lm_head_kernel_name(cfg)
+    roof["kernel"] = (f"fdl_lm_head_select ({kname} with the select epilogue + select_finalize_kernel)"
+                      if run.fused else f"fdl_lm_head ({kname})")
     roof["kernel_us"] = lm_ms * 1e3
     roof["algorithmic_bytes"] = byts
 
