@@ -303,13 +303,16 @@ __global__ __launch_bounds__(256) void lm_head_skinny_f32(LmArgs a) {
 // ---------------------------------------------------------------------------
 // tiled (M > 64): workgroup tile 256 (vocab) x 256 (rows), 8 waves in a 2 x 4
 // grid of 128 x 64 wave tiles (4 x 2 MFMA 32x32x16 tiles each).  K is consumed
-// in 32-wide slabs that travel HBM -> LDS by global_load_lds_dwordx4 (no
-// register staging) through a TB_NST-stage ring, three slabs ahead of the
-// MFMA work.  A slab row is 64 bytes = 4 chunks of 16; chunk c of row r sits
-// at chunk c ^ ((r >> 2) & 3) so that the 32-row fragment reads of a wave are
-// free of bank conflicts.  Fragment reads are software-pipelined: the eight
-// MFMAs of one 16-wide k-step run while the next k-step's fragments are read.
-constexpr int TB_V = 256, TB_M = 256, TB_K = 32, TB_NST = 5, TB_NWV = 2, TB_NWM = 4;  // 5 x 32 KB: all of LDS
+// in 64-wide slabs that travel HBM -> LDS by global_load_lds_dwordx4 (no
+// register staging) through two 64 KB stages: the next slab's loads are in
+// flight while the current slab is consumed, one barrier per slab.  A slab
+// row is 128 bytes = 8 chunks of 16; chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7) so that the 32-row fragment reads of a wave are free of
+// bank conflicts.  Fragment reads are software-pipelined: the eight MFMAs of
+// one 16-wide k-step run while the next k-step's fragments are read (against
+// 32-wide slabs in a five-stage ring: 624 -> 561 us for M = 512, half the
+// barriers).
+constexpr int TB_V = 256, TB_M = 256, TB_K = 64, TB_NST = 2, TB_NWV = 2, TB_NWM = 4;  // 2 x 64 KB of LDS
 constexpr int TB_ROWB = TB_K * 2;                          // bytes per row per stage
 constexpr int TB_ABYTES = TB_V * TB_ROWB, TB_STB = (TB_V + TB_M) * TB_ROWB;
 constexpr int TB_NT = TB_NWV * TB_NWM * 64;
@@ -366,17 +369,18 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
 
-  // Load instruction j of this wave fills stage bytes [kb KB, kb KB + 1 KB),
-  // 16 rows (W rows 0..255, then X rows): lane l writes physical chunk l & 3
-  // of row kb * 16 + l / 4, which holds logical chunk (l & 3) ^ ((row >> 2) & 3).
-  // Rows past V or M read a valid row; their results are never stored.
+  // Load instruction j of this wave fills stage bytes [kb KB, kb KB + 1 KB):
+  // 8 rows of 128 bytes (W rows 0..255, then X rows); lane l writes physical
+  // chunk l & 7 of row kb * 8 + l / 8, which holds logical chunk
+  // (l & 7) ^ ((row >> 1) & 7).  Rows past V or M read a valid row; their
+  // results are never stored.
   const bf16_t* src[TB_IPW];
   int dst[TB_IPW];
 #pragma unroll
   for (int j = 0; j < TB_IPW; ++j) {
     const int kb = wave * TB_IPW + j;
-    const int rr = kb * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((rr >> 2) & 3);
+    const int rr = kb * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((rr >> 1) & 7);
     if (rr < TB_V) src[j] = W + size_t(min(v0 + rr, a.V - 1)) * a.H + c * 8;
     else src[j] = X + size_t(min(m0 + rr - TB_V, a.M - 1)) * a.H + c * 8;
     dst[j] = kb * 1024;
@@ -398,9 +402,7 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = a.H / TB_K;
-#pragma unroll
-  for (int s = 0; s < TB_NST - 2; ++s)
-    if (s < nk) issue(s);
+  issue(0);
   // the fragments of one 16-wide k-step of a slab
   auto frag = [&](int slab, int ks, u32x4* af, u32x4* bf) __attribute__((always_inline)) {
     const char* sb = smem + (slab % TB_NST) * TB_STB;
@@ -410,12 +412,12 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
 #pragma unroll
     for (int i = 0; i < TB_TV; ++i) {
       const int r = wv0 + i * 32 + l32;
-      af[i] = *reinterpret_cast<const u32x4*>(As + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
+      af[i] = *reinterpret_cast<const u32x4*>(As + r * TB_K + 8 * (c ^ ((r >> 1) & 7)));
     }
 #pragma unroll
     for (int j = 0; j < TB_TM; ++j) {
       const int r = wm0 + j * 32 + l32;
-      bf[j] = *reinterpret_cast<const u32x4*>(Bs + r * TB_K + 8 * (c ^ ((r >> 2) & 3)));
+      bf[j] = *reinterpret_cast<const u32x4*>(Bs + r * TB_K + 8 * (c ^ ((r >> 1) & 7)));
     }
   };
   auto mma = [&](const u32x4* af, const u32x4* bf) __attribute__((always_inline)) {
@@ -424,12 +426,10 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
 #pragma unroll
       for (int j = 0; j < TB_TM; ++j) acc[i][j] = mfma32x32x16_bf16(af[i], bf[j], acc[i][j]);
   };
-  // slab t has landed once this wave's own loads of it are done (at most the
-  // two later slabs' loads in flight) and, after the barrier, every wave's.
-  // A bare barrier: __syncthreads() would also wait for the later loads.
-  auto arrive = [&](int t) __attribute__((always_inline)) {
-    if (t + TB_NST - 3 < nk) wait_vmcnt<(TB_NST - 3) * TB_IPW>();
-    else wait_vmcnt<0>();
+  // a slab has landed once this wave's own loads of it are done and, after
+  // the barrier, every wave's
+  auto arrive = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
   };
   // Each group of eight MFMAs runs while the next k-step's fragments are
@@ -438,9 +438,10 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
   // no wait of its own in front of the next group; every loop iteration has
   // the same shape (the last slab is peeled) so its wait counts stay exact.
   constexpr int LGKM0 = 0xC07F;  // s_waitcnt lgkmcnt(0), the other counters untouched
+  static_assert(TB_K == 64, "four k-steps per slab below");
   u32x4 a0[TB_TV], b0[TB_TM], a1[TB_TV], b1[TB_TM];
-  arrive(0);
-  if (TB_NST - 2 < nk) issue(TB_NST - 2);
+  arrive();
+  if (1 < nk) issue(1);
   frag(0, 0, a0, b0);
   __builtin_amdgcn_s_waitcnt(LGKM0);
   for (int t = 0; t + 1 < nk; ++t) {
@@ -449,18 +450,33 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
     mma(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(LGKM0);
-    arrive(t + 1);
+    frag(t, 2, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(LGKM0);
+    frag(t, 3, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(LGKM0);
+    arrive();                       // slab t + 1 has landed everywhere
+    if (t + 2 < nk) issue(t + 2);   // into slab t's stage: every wave read and waited for it above
     frag(t + 1, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     mma(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(LGKM0);
-    // the buffer refilled here held slab t - 1, whose fragments every wave
-    // read and waited for before the barrier above
-    if (t + TB_NST - 1 < nk) issue(t + TB_NST - 1);
   }
   frag(nk - 1, 1, a1, b1);
   mma(a0, b0);
+  __builtin_amdgcn_s_waitcnt(LGKM0);
+  frag(nk - 1, 2, a0, b0);
+  mma(a1, b1);
+  __builtin_amdgcn_s_waitcnt(LGKM0);
+  frag(nk - 1, 3, a1, b1);
+  mma(a0, b0);
+  __builtin_amdgcn_s_waitcnt(LGKM0);
   mma(a1, b1);
 
   // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile; a
