@@ -206,84 +206,109 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   }
 }
 
-// Many rows (B x R > 64, R a multiple of 8, R <= 64): a workgroup of 1024
-// threads merges 8 rows of one sequence, 128 threads per row with sixteen
-// partial loads in flight per thread (thread t of a row takes partials t,
-// t + 128, ... in increasing order; then a fixed butterfly over the wave and
-// the row's two waves in order), writes their tokens and confidences and
-// counts itself on the sequence's counter: R / 8 arrivals per counter instead
-// of R, since device-scope atomics on one address serialize and each
-// arrival's release fence is a write-back of the CU's L2 (measured at 16 x 32
-// rows: 25 us per-row, 17 us without the fences, 8 us for the merges alone).
-// The workgroup that counts a sequence's last group applies the rule in one
-// wave, lane q = row q, with the same decisions as select_finalize_kernel.
-constexpr int FGR_NT = 1024, FGR_ROWS = 8, FGR_T = FGR_NT / FGR_ROWS, FGR_U = 16;
-static_assert(FGR_T == 128, "two waves per row below");
+// One workgroup of 1024 threads per sequence (R <= 64 rows), TPR threads per
+// row: no device-scope synchronization at all.  Wave 0 fetches the rule's
+// inputs (masked flags, tau) before the partials arrive.  Phase 1: each
+// thread merges its share of the row's partials (max and lowest argmax first,
+// then one exponential per partial), then a fixed xor butterfly over the
+// row's lanes -- every lane ends with the same bits -- and, for rows wider
+// than a wave, a fixed combination of the row's waves.  Phase 2: wave 0, lane
+// q = row q, applies the rule from LDS, with the decisions of
+// select_finalize_kernel.
+constexpr int FSQ_NT = 1024, FSQ_U = 16;
 
-__global__ __launch_bounds__(FGR_NT) void select_finalize_group_kernel(SelArgs a) {
-  __shared__ Red red_w[FGR_NT / 64];
-  __shared__ float conf_s[64];
-  __shared__ int tok_s[64];
-  __shared__ int cand_s[64];
-  __shared__ int last_s;
+// U partials of one thread (empty ones: -inf, 0, INT_MAX) -> (max, lowest
+// argmax, sum of s exp(m - max))
+template <int U>
+__device__ __forceinline__ Red merge_run(const f32x4 (&p)[U]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) mx = fmaxf(mx, p[u][0]);
+  int im = INT_MAX;
+  float sm = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const Red q = unpack_red(p[u]);
+    if (q.m == mx) im = min(im, q.i);
+    if (q.s > 0.f) sm += q.s * exp2f((q.m - mx) * kLog2e);
+  }
+  return Red{mx, sm, im};
+}
+
+// xor butterfly over groups of W lanes (W a power of two up to 64)
+template <int W>
+__device__ __forceinline__ Red butterfly_red(Red r) {
+  float mx = r.m;
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  int im = r.m == mx ? r.i : INT_MAX;
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) im = min(im, __shfl_xor(im, o, kWave));
+  float sm = r.s > 0.f ? r.s * exp2f((r.m - mx) * kLog2e) : 0.f;
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) sm += __shfl_xor(sm, o, kWave);
+  return Red{mx, sm, im};
+}
+
+template <int TPR>
+__global__ __launch_bounds__(FSQ_NT) void select_finalize_seq_kernel(SelArgs a) {
+  constexpr int ROWS = FSQ_NT / TPR, WPR = TPR > kWave ? TPR / kWave : 1;
+  static_assert(ROWS <= 64, "one lane of wave 0 per row in the rule phase");
+  __shared__ Red wred[FSQ_NT / kWave];
+  __shared__ float conf_s[ROWS];
+  __shared__ int tok_s[ROWS];
+  __shared__ int cand_s[ROWS];
   if (gate_closed(a.gate)) return;
-  const int ngrp = a.R / FGR_ROWS;
-  const int b = blockIdx.x / ngrp, r0 = (blockIdx.x % ngrp) * FGR_ROWS;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int r = r0 + tid / FGR_T, t = tid % FGR_T;
-  {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = tid / TPR, t = tid % TPR;
+  const int q = lane;  // the row of this lane in the rule phase
+  const bool live = wave == 0 && q < a.R;
+  const size_t srow = size_t(b) * a.sstride + q;
+  bool cand = false;
+  float tau = 0.f;
+  if (live) cand = a.masked[srow] != 0;
+  if (wave == 0 && a.mode == FDL_SELECT_THRESHOLD) tau = a.tau[b];
+
+  Red acc = red_empty();
+  if (r < a.R) {
     const f32x4* prow = a.part + (size_t(b) * a.R + r) * a.NC;
-    Red acc = red_empty();
-    for (int c0 = t; c0 < a.NC; c0 += FGR_T * FGR_U) {
-      f32x4 p[FGR_U];
+    for (int c0 = t; c0 < a.NC; c0 += TPR * FSQ_U) {
+      f32x4 p[FSQ_U];
 #pragma unroll
-      for (int u = 0; u < FGR_U; ++u) {
-        const int c = c0 + u * FGR_T;
-        p[u] = c < a.NC ? prow[c] : f32x4{-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
+      for (int u = 0; u < FSQ_U; ++u) {
+        const int c = c0 + u * TPR;
+        p[u] = c < a.NC ? prow[c] : f32x4{-INFINITY, 0.f, __int_as_float(INT_MAX), 0.f};
       }
-#pragma unroll
-      for (int u = 0; u < FGR_U; ++u) acc = combine(acc, unpack_red(p[u]));
+      acc = combine(acc, merge_run(p));
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) acc = combine(acc, shfl_xor_red(acc, o));
-    if (lane == 0) red_w[tid >> 6] = acc;
+  }
+  acc = butterfly_red<(TPR < kWave ? TPR : kWave)>(acc);
+  if (WPR > 1) {
+    if (lane == 0) wred[wave] = acc;
     __syncthreads();
     if (t == 0) {
-      const Red res = combine(red_w[tid >> 6], red_w[(tid >> 6) + 1]);
-      const size_t row = size_t(b) * a.R + r;
-      a.token_out[row] = res.i;
-      a.conf_out[row] = 1.f / res.s;
+      Red w = wred[wave];
+      for (int j = 1; j < WPR; ++j) w = combine(w, wred[wave + j]);
+      acc = w;
     }
-    // the group's rows are written (the barrier waits for every wave's
-    // stores); one release and one count for the whole group
-    __syncthreads();
-    if (tid == 0) {
-      __threadfence();
-      last_s = atomicAdd(&a.cnt[b], 1) == ngrp - 1;
-    }
-    __syncthreads();
-    if (!last_s) return;
-    __threadfence();
   }
-  if (tid >= 64) return;
-  const int q = tid;
-  const bool live = q < a.R;
+  if (t == 0 && r < a.R) {
+    conf_s[r] = 1.f / acc.s;
+    tok_s[r] = acc.i;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
   const size_t row = size_t(b) * a.R + q;
-  const size_t srow = size_t(b) * a.sstride + q;
   float conf = 0.f;
-  int tok = 0;
-  bool cand = false;
   if (live) {
-    conf = __hip_atomic_load(&a.conf_out[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tok = __hip_atomic_load(&a.token_out[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    cand = a.masked[srow] != 0;
-    conf_s[q] = conf;
+    conf = conf_s[q];
     cand_s[q] = cand;
-    tok_s[q] = tok;
   }
   __builtin_amdgcn_wave_barrier();
   int rank = 0;  // among candidates: decreasing confidence, lower row first on ties
-  if (cand) {
+  if (live && cand) {
     for (int p = 0; p < a.R; ++p) {
       if (!cand_s[p]) continue;
       const float cp = conf_s[p];
@@ -292,16 +317,106 @@ __global__ __launch_bounds__(FGR_NT) void select_finalize_group_kernel(SelArgs a
   }
   bool sel = false;
   if (a.mode == FDL_SELECT_THRESHOLD) {
-    sel = cand && conf > a.tau[b];
-    if (__builtin_amdgcn_ballot_w64(sel) == 0) sel = cand && rank == 0;  // fallback: the most confident candidate
+    sel = live && cand && conf > tau;
+    if (__builtin_amdgcn_ballot_w64(sel) == 0) sel = live && cand && rank == 0;  // fallback: the most confident
   } else if (a.mode == FDL_SELECT_TOPK) {
-    sel = cand && rank < a.k;
+    sel = live && cand && rank < a.k;
   } else {  // FDL_SELECT_FACTOR
     const int n = rank + 1;
-    int best = cand && float(n + 1) * (1.f - conf) < a.factor ? n : 0;
+    int best = live && cand && float(n + 1) * (1.f - conf) < a.factor ? n : 0;
     for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, kWave));
     const int nstar = best > 0 ? best : 1;
-    sel = cand && rank < nstar;
+    sel = live && cand && rank < nstar;
+  }
+  const int n_sel = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sel));
+  if (q == 0) a.n_commit[b] = n_sel;
+  if (live) {
+    a.token_out[row] = tok_s[q];
+    a.conf_out[row] = conf;
+    a.commit_out[row] = sel ? 1 : 0;
+    if (sel && a.tokens_inout) a.tokens_inout[srow] = tok_s[q];
+    if (sel && a.masked_inout) a.masked_inout[srow] = 0;
+  }
+}
+
+// One wave per row (R <= 64): the row's partials, FRW_U per lane in flight,
+// merged as above with one butterfly; lane 0 writes the row's token and
+// confidence and counts the row on its sequence's counter (zeroed by the
+// producer of the partials), and the wave that counts the sequence's last row
+// applies the rule, lane q = row q.  The rule's masked flags and tau are
+// fetched at the start by every wave, so the last one only reloads the
+// sequence's tokens and confidences.  No workgroup barrier anywhere.
+constexpr int FRW_U = 20;
+
+__global__ __launch_bounds__(kWave) void select_finalize_row_kernel(SelArgs a) {
+  __shared__ float conf_s[64];
+  __shared__ int cand_s[64];
+  if (gate_closed(a.gate)) return;
+  const int row_g = blockIdx.x;  // b * R + r
+  const int b = row_g / a.R;
+  const int lane = threadIdx.x;
+  const int q = lane;
+  const bool live = q < a.R;
+  const size_t srow = size_t(b) * a.sstride + q;
+  bool cand = false;
+  float tau = 0.f;
+  if (live) cand = a.masked[srow] != 0;
+  if (a.mode == FDL_SELECT_THRESHOLD) tau = a.tau[b];
+
+  Red acc = red_empty();
+  const f32x4* prow = a.part + size_t(row_g) * a.NC;
+  for (int c0 = lane; c0 < a.NC; c0 += kWave * FRW_U) {
+    f32x4 p[FRW_U];
+#pragma unroll
+    for (int u = 0; u < FRW_U; ++u) {
+      const int c = c0 + u * kWave;
+      p[u] = c < a.NC ? prow[c] : f32x4{-INFINITY, 0.f, __int_as_float(INT_MAX), 0.f};
+    }
+    acc = combine(acc, merge_run(p));
+  }
+  acc = butterfly_red<kWave>(acc);
+  int prev = 0;
+  if (lane == 0) {
+    a.token_out[row_g] = acc.i;
+    a.conf_out[row_g] = 1.f / acc.s;
+    // publish the row, then count it
+    __threadfence();
+    prev = atomicAdd(&a.cnt[b], 1);
+  }
+  prev = __shfl(prev, 0, kWave);
+  if (prev != a.R - 1) return;
+  __threadfence();
+
+  const size_t row = size_t(b) * a.R + q;
+  float conf = 0.f;
+  int tok = 0;
+  if (live) {
+    conf = __hip_atomic_load(&a.conf_out[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tok = __hip_atomic_load(&a.token_out[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    conf_s[q] = conf;
+    cand_s[q] = cand;
+  }
+  __builtin_amdgcn_wave_barrier();
+  int rank = 0;  // among candidates: decreasing confidence, lower row first on ties
+  if (live && cand) {
+    for (int p = 0; p < a.R; ++p) {
+      if (!cand_s[p]) continue;
+      const float cp = conf_s[p];
+      rank += (cp > conf || (cp == conf && p < q)) ? 1 : 0;
+    }
+  }
+  bool sel = false;
+  if (a.mode == FDL_SELECT_THRESHOLD) {
+    sel = live && cand && conf > tau;
+    if (__builtin_amdgcn_ballot_w64(sel) == 0) sel = live && cand && rank == 0;  // fallback: the most confident
+  } else if (a.mode == FDL_SELECT_TOPK) {
+    sel = live && cand && rank < a.k;
+  } else {  // FDL_SELECT_FACTOR
+    const int n = rank + 1;
+    int best = live && cand && float(n + 1) * (1.f - conf) < a.factor ? n : 0;
+    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, kWave));
+    const int nstar = best > 0 ? best : 1;
+    sel = live && cand && rank < nstar;
   }
   const int n_sel = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sel));
   if (q == 0) {
@@ -310,16 +425,32 @@ __global__ __launch_bounds__(FGR_NT) void select_finalize_group_kernel(SelArgs a
   }
   if (live) {
     a.commit_out[row] = sel ? 1 : 0;
-    if (sel && a.tokens_inout) a.tokens_inout[srow] = tok_s[q];
+    if (sel && a.tokens_inout) a.tokens_inout[srow] = tok;
     if (sel && a.masked_inout) a.masked_inout[srow] = 0;
   }
 }
 
+// Up to 256 rows: one wave per row, so that the partials stream through as
+// many CUs as there are rows (measured at 1278 partials per row: 4 x 8 rows
+// 8.2 -> 6.5 us, 1 x 32 rows 9.9 -> 8.1 us against the 256-thread per-row
+// kernel).  More rows (and R <= 64): one workgroup per sequence, no
+// device-scope synchronization (16 x 32 rows of 1188 partials: 21.9 ->
+// 12.9 us).  R > 64: the 256-thread per-row kernel.
 static void launch_finalize(const SelArgs& a, hipStream_t st) {
-  if (a.B * a.R > 64 && a.R % FGR_ROWS == 0 && a.R <= 64)
-    hipLaunchKernelGGL(select_finalize_group_kernel, dim3(a.B * (a.R / FGR_ROWS)), dim3(FGR_NT), 0, st, a);
-  else
+  if (a.R > 64) {
     hipLaunchKernelGGL(select_finalize_kernel, dim3(a.B * a.R), dim3(FIN_NT), 0, st, a);
+  } else if (a.B * a.R <= 256) {
+    hipLaunchKernelGGL(select_finalize_row_kernel, dim3(a.B * a.R), dim3(kWave), 0, st, a);
+  } else {
+    int rp2 = 1;
+    while (rp2 < a.R) rp2 *= 2;
+    switch (FSQ_NT / rp2) {  // threads per row
+      case 16: hipLaunchKernelGGL(select_finalize_seq_kernel<16>, dim3(a.B), dim3(FSQ_NT), 0, st, a); break;
+      case 32: hipLaunchKernelGGL(select_finalize_seq_kernel<32>, dim3(a.B), dim3(FSQ_NT), 0, st, a); break;
+      case 64: hipLaunchKernelGGL(select_finalize_seq_kernel<64>, dim3(a.B), dim3(FSQ_NT), 0, st, a); break;
+      default: hipLaunchKernelGGL(select_finalize_seq_kernel<128>, dim3(a.B), dim3(FSQ_NT), 0, st, a); break;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
