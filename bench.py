@@ -60,6 +60,14 @@ def lm_head_kernel_name(cfg):
     return "lm_head_skinny_bf16" if cfg.rows <= 64 else "lm_head_tiled_bf16"
 
 
+def finalize_kernel_name(cfg):
+    """The select finalize kernel the library launches after the fused LM head."""
+    r, rows = cfg.rows // cfg.batch, cfg.rows
+    if r > 64:
+        return "select_finalize_kernel"
+    return "select_finalize_row_kernel" if rows <= 256 else "select_finalize_seq_kernel"
+
+
 def pmc_traffic(workload, per_launch_units=1):
     """HBM bytes per launch from the committed rocprofv3 counter summary, scaled
     by the copy-kernel calibration; None when missing, taken on another
@@ -299,7 +307,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = pmc_traffic(cfg.name) if run.fused else None
     kname = lm_head_kernel_name(cfg)
-    roof["kernel"] = (f"fdl_lm_head_select ({kname} with the select epilogue + select_finalize_kernel)"
+    roof["kernel"] = (f"fdl_lm_head_select ({kname} with the select epilogue + {finalize_kernel_name(cfg)})"
                       if run.fused else f"fdl_lm_head ({kname})")
     roof["kernel_us"] = lm_ms * 1e3
     roof["algorithmic_bytes"] = byts
