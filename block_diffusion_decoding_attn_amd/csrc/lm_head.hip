@@ -22,7 +22,8 @@ struct LmArgs {
   const void* x;
   const void* w;
   float* out;    // [M][V] logits, or null (fused select: only partials)
-  f32x4* part;   // [M][nc] confidence partials, one per workgroup vocabulary span, or null
+  f32x4* part;   // [M][nc] confidence partials (one per workgroup vocabulary span: skinny span or
+                 // 256-row weight tile), or null
   int M, H, V, nc;
   const int32_t* gate;  // decode loop: skip the launch when *gate == 0 (null: always run)
   int32_t* cnt;         // select row counters to zero (with part), or null
@@ -318,7 +319,7 @@ constexpr int TB_ABYTES = TB_V * TB_ROWB, TB_STB = (TB_V + TB_M) * TB_ROWB;
 constexpr int TB_NT = TB_NWV * TB_NWM * 64;
 constexpr int TB_IPW = TB_STB / 1024 / (TB_NWV * TB_NWM);  // 1 KB load instructions per wave per stage
 constexpr int TB_TV = TB_V / TB_NWV / 32, TB_TM = TB_M / TB_NWM / 32;
-static_assert(TB_TV * 32 == 128, "a wave covers one 128-row vocabulary tile of the select partials");
+static_assert(TB_TV * 32 == 128, "a wave covers half of a 256-row weight tile");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -479,9 +480,13 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
   __builtin_amdgcn_s_waitcnt(LGKM0);
   mma(a1, b1);
 
-  // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile; a
-  // wave's 128 vocabulary rows are exactly one tile of the select partials
-  if (a.part && v0 + wv0 < a.V) {
+  // lane holds C[vocab 8(e/4) + 4 half + e%4][row l32] of each 32x32 tile.
+  // The two waves of a row band (wave % TB_NWV = 0, 1) hold the lower and
+  // upper 128 vocabulary rows of the weight tile: the upper one hands its
+  // partials over through LDS and the lower one writes the tile's partial,
+  // lower rows first (one partial per row and 256-row weight tile).
+  if (a.part) {
+    Red rr[TB_TM];
 #pragma unroll
     for (int j = 0; j < TB_TM; ++j) {
       Red r = red_empty();
@@ -490,9 +495,23 @@ __global__ __launch_bounds__(TB_NT) void lm_head_tiled_bf16(LmArgs a) {
         __builtin_amdgcn_sched_barrier(0);  // one accumulator tile at a time
         r = combine(r, tile_red(acc[i][j], v0 + wv0 + i * 32 + half * 4, a.V));
       }
-      r = combine(r, shfl_xor_red(r, 32));
-      const int m = m0 + wm0 + j * 32 + l32;
-      if (half == 0 && m < a.M) a.part[size_t(m) * a.nc + (v0 + wv0) / 128] = pack_red(r);
+      rr[j] = combine(r, shfl_xor_red(r, 32));
+    }
+    static_assert(TB_NWV == 2 && TB_TM * 32 * TB_NWM * 16 <= TB_NST * TB_STB, "partials hand-over in LDS");
+    f32x4* xch = reinterpret_cast<f32x4*>(smem);  // [row band][TB_TM * 32 rows]
+    __syncthreads();                               // every wave is done with the K slabs
+    if (wave % TB_NWV == 1 && half == 0) {
+#pragma unroll
+      for (int j = 0; j < TB_TM; ++j) xch[(wave / TB_NWV) * (TB_TM * 32) + j * 32 + l32] = pack_red(rr[j]);
+    }
+    __syncthreads();
+    if (wave % TB_NWV == 0 && half == 0) {
+#pragma unroll
+      for (int j = 0; j < TB_TM; ++j) {
+        const Red r = combine(rr[j], unpack_red(xch[(wave / TB_NWV) * (TB_TM * 32) + j * 32 + l32]));
+        const int m = m0 + wm0 + j * 32 + l32;
+        if (m < a.M) a.part[size_t(m) * a.nc + vt] = pack_red(r);
+      }
     }
   }
   if (!a.out) return;
@@ -550,8 +569,11 @@ static void launch_skinny_f32(const LmArgs& a, hipStream_t st) {
 }
 
 int lm_head_tiles(const fdl_dims& d, int rows) {
-  if (d.dtype == FDL_BF16 && rows <= 64) return skinny_workgroups(d.vocab, rows);
-  return (d.vocab + 127) / 128;  // tiled kernel and f32: one partial per 128-row vocabulary tile
+  if (d.dtype == FDL_BF16) {
+    if (rows <= 64) return skinny_workgroups(d.vocab, rows);
+    return (d.vocab + TB_V - 1) / TB_V;  // tiled: one partial per 256-row weight tile
+  }
+  return (d.vocab + 127) / 128;  // f32: one partial per 128-row vocabulary tile
 }
 
 int lm_head_launch(const fdl_dims& d, int rows, const void* x, const void* w, float* logits, void* part,

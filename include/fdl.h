@@ -202,8 +202,9 @@ int fdl_conf_select(const fdl_dims* dims, int32_t rows_per_seq, const float* log
 
 /* Bytes of device workspace fdl_lm_head_select needs: 16 bytes per (row,
  * vocabulary span) of select partials -- a span is the vocabulary range of
- * one LM-head workgroup: 128 rows, or V / 1280 rounded up for up to 32 rows
- * and a vocabulary of 81,920 to 163,840 -- then one 4-byte row counter per
+ * one LM-head workgroup: for bf16 and up to 64 rows 128 rows, or V / 1280
+ * rounded up for up to 32 rows and a vocabulary of 81,920 to 163,840; for
+ * bf16 and more rows 256; for f32 128 -- then one 4-byte row counter per
  * sequence (rounded up to 16 bytes).  0 for invalid arguments.  The
  * workspace is scratch of one call: calls that overlap on it race. */
 size_t fdl_lm_head_select_workspace_size(const fdl_dims* dims, int32_t rows_per_seq);
