@@ -11,8 +11,8 @@
 //     staged with the matching X slab through LDS, and fed to MFMA
 //     (A = W rows, B = X^T).
 //   * tiled (M > 64): MFMA-bound; 256 x 256 output tiles per workgroup, K
-//     streamed HBM -> LDS by direct-to-LDS loads through a 4-stage ring,
-//     32x32x16 bf16 MFMA.
+//     streamed HBM -> LDS by direct-to-LDS loads through two 64-wide slab
+//     stages, 32x32x16 bf16 MFMA.
 #include "common.h"
 #include "launch.h"
 

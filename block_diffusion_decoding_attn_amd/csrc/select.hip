@@ -13,10 +13,12 @@
 // every row into chunks so that thousands of workgroups stream it with 16-byte
 // loads, each reducing its chunk to (max, lowest argmax, sum exp(l - max)).
 // (The fused LM head writes the same partials from its epilogue instead.)
-// Kernel 2 (one workgroup per row) merges a row's partials in a fixed order --
-// the result does not depend on scheduling -- and the workgroup that finishes
-// a sequence's last row applies the selection rule, then writes the commit set
-// and updates tokens/masked.
+// Kernel 2, the finalize, merges a row's partials in a fixed order -- the
+// result does not depend on scheduling -- and applies the selection rule per
+// sequence, then writes the commit set and updates tokens/masked: one wave
+// per row (the wave that counts a sequence's last row applies the rule) up to
+// 256 rows, one workgroup per sequence beyond that, or, for more than 64 rows
+// per sequence, one 256-thread workgroup per row.
 #include <climits>
 
 #include "common.h"
