@@ -190,6 +190,22 @@ def test_decode_rerun_is_identical():
     assert first["steps"] == second["steps"]
 
 
+@pytest.mark.parametrize("select", ["threshold", "factor"])
+def test_decode_many_rows_bf16(select):
+    """bf16, 9 sequences x 32 rows per step: inside the loop the LM head takes
+    its tiled path (more than 64 rows, a partial second row tile) and the
+    select its one-workgroup-per-sequence finalize (more than 256 rows)."""
+    _need_gpu()
+    print(f"decode many rows bf16 {select}", flush=True)
+    cfg = _tiny(dtype="bf16", batch=9, gen_len=64, sub_block=32)
+    assert cfg.rows == 288
+    run = DecodeRunner(cfg, seed=3, select=select, k=4, factor=1.0)
+    run.run()
+    torch.cuda.synchronize()
+    res = _compare(run, run.results(), _oracle(run))
+    assert res["forked"] is None or res["forked"] >= 10
+
+
 @pytest.mark.parametrize("name,max_blocks", [("qwen2.5-1.5b_bs1", 2), ("qwen2.5-7b_bs4", 1),
                                              ("llada-8b_dualcache", 1)])
 def test_decode_workload_shapes_bf16(name, max_blocks):
