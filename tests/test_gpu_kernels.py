@@ -68,6 +68,11 @@ def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
     (dict(n_q_heads=20, n_kv_heads=4, sub_block=32, batch=1, prompt_len=1000, gen_len=64), 1, None),  # 160 rows
     (dict(n_q_heads=28, n_kv_heads=4, sub_block=32, batch=8, prompt_len=1440, gen_len=96), 2, None),  # 3-tile splits
     (dict(attn_mode=synth.DUAL_CACHE, n_q_heads=8, n_kv_heads=1, sub_block=32), 1, None),    # DualCache, 256 rows
+    # at most 64 rows per KV head, several splits with empty ones, DualCache, d 64
+    (dict(n_q_heads=4, n_kv_heads=4, sub_block=32, batch=3, prompt_len=700, gen_len=64), 1, [700, 3, 731]),
+    (dict(attn_mode=synth.DUAL_CACHE, n_q_heads=8, n_kv_heads=4, sub_block=32), 1, None),    # DualCache, 64 rows
+    (dict(head_dim=64, n_q_heads=2, n_kv_heads=2, sub_block=16), 2, None),                   # d 64, 16 rows
+    (dict(n_q_heads=1, n_kv_heads=1, sub_block=8, prompt_len=190, gen_len=64), 0, None),     # 8 rows, 4 tiles
 ])
 def test_block_attn_parity(kw, block_idx, prefix):
     cfg = _cfg(**kw)
