@@ -116,6 +116,31 @@ def test_entry_points_reject_before_launch(L):
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 32, None, None) == -1
 
 
+def test_workspace_too_small_rejected(L):
+    """A missing or short workspace returns FDL_E_WORKSPACE before any launch."""
+    d = _dims()
+    P = ctypes.c_void_p
+    fake = P(16)
+    by = ctypes.byref
+    args = [fake, fake, fake, fake]
+    # the 7B/bs4 step splits its keys, so block attention needs partials space
+    assert fdl.fdl_block_attn_workspace_size(d) > 0
+    assert L.fdl_block_attn(by(d), 0, 0, fake, fake, fake, None, fake, fake, fake, None, None, 0, None) == -4
+    assert L.fdl_block_attn(by(d), 15, 3, fake, fake, fake, None, fake, fake, fake, None, fake, 64, None) == -4
+    need = fdl.fdl_conf_select_workspace_size(d, 8)
+    assert L.fdl_conf_select(by(d), 8, fake, fake, fake, 0, 0, 0.0, *args, None, None, fake, need - 1, None) == -4
+    assert L.fdl_conf_select(by(d), 8, fake, fake, fake, 0, 0, 0.0, *args, None, None, None, need, None) == -4
+    need = fdl.fdl_lm_head_select_workspace_size(d, 8)
+    assert need >= 32 * 16
+    assert L.fdl_lm_head_select(by(d), 8, fake, fake, None, fake, fake, 0, 0, 0.0, *args, None, None, fake,
+                                need - 1, None) == -4
+    assert L.fdl_lm_head_select(by(d), 8, fake, fake, None, fake, fake, 0, 0, 0.0, *args, None, None, None,
+                                need, None) == -4
+    # the long-context shape: the tiled LM head keeps one partial per 256-row weight tile
+    dl = _dims("qwen2.5-7b_long_bs16")
+    assert fdl.fdl_lm_head_select_workspace_size(dl, 32) >= 16 * 32 * ((152064 + 255) // 256) * 16
+
+
 def _decode_args(**over):
     fake = 16
     a = fdl.fdl_decode_args(w=fake, gain=2.0, mask_id=10, eos_id=11, prompt=fake, boost_tok=fake, boost_val=fake,
