@@ -216,6 +216,16 @@ int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void
   return append_launch(d, k_cache, v_cache, k_new, v_new, n_new, len, reinterpret_cast<hipStream_t>(stream));
 }
 
+int fdl_kv_write(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                 int32_t pos, int32_t n_new, int32_t* len, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  if (!k_cache || !v_cache || !k_new || !v_new) return FDL_E_INVAL;
+  if (n_new < 1 || pos < 0 || (long long)pos + n_new > (long long)d.prompt_len + d.gen_len) return FDL_E_INVAL;
+  return write_launch(d, k_cache, v_cache, k_new, v_new, pos, n_new, len, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t fdl_decode_workspace_size(const fdl_dims* dims) {
   if (check_dims(dims) != FDL_OK) return 0;
   return decode_workspace_bytes(*dims);

@@ -48,6 +48,34 @@ __global__ void kv_append_len_kernel(int32_t* len, int B, int cap, int n_new, co
   len[b] = lo + n_new;
 }
 
+// Write at a position given by the caller (the refresh: every position from
+// 0): the copies do not read len, so workgroup (0, 0, b) sets it directly and
+// one launch does the whole step.
+__global__ __launch_bounds__(256) void kv_write_kernel(AppendArgs a, int pos) {
+  const int b = blockIdx.z;
+  const int kv = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
+  const size_t pair = size_t(b) * a.Hkv + g;
+  const char* src = reinterpret_cast<const char*>(kv ? a.vn : a.kn) + pair * a.n_new * size_t(a.row_bytes);
+  char* dst = reinterpret_cast<char*>(kv ? a.vc : a.kc) + (pair * a.cap + pos) * size_t(a.row_bytes);
+  const size_t n16 = size_t(a.n_new) * a.row_bytes / 16;
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
+    st16(dst + i * 16, ld16(src + i * 16));
+  if (a.len && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.len[b] = pos + a.n_new;
+}
+
+int write_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int pos, int n_new,
+                 int32_t* len, hipStream_t st) {
+  AppendArgs a;
+  a.kc = kc; a.vc = vc; a.kn = kn; a.vn = vn; a.len = len; a.gate = nullptr;
+  a.B = d.batch; a.Hkv = d.n_kv_heads; a.cap = d.prompt_len + d.gen_len; a.n_new = n_new;
+  a.row_bytes = d.head_dim * dtype_size(d.dtype);
+  const size_t n16 = size_t(n_new) * a.row_bytes / 16;
+  int chunks = int((n16 + 255) / 256);
+  if (chunks > 64) chunks = 64;
+  hipLaunchKernelGGL(kv_write_kernel, dim3(chunks, 2 * d.n_kv_heads, d.batch), dim3(256), 0, st, a, pos);
+  return check_launch();
+}
+
 int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int n_new, int32_t* len,
                   hipStream_t st, const int32_t* gate) {
   AppendArgs a;

@@ -32,6 +32,8 @@ int select_launch(const fdl_dims& d, int R, const float* logits, const uint8_t* 
                   int32_t* tokens_inout, uint8_t* masked_inout, void* ws, size_t ws_bytes, hipStream_t st);
 int append_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int n_new, int32_t* len,
                   hipStream_t st, const int32_t* gate = nullptr);
+int write_launch(const fdl_dims& d, void* kc, void* vc, const void* kn, const void* vn, int pos, int n_new,
+                 int32_t* len, hipStream_t st);
 size_t decode_workspace_bytes(const fdl_dims& d);
 int decode_slots_per_sub(const fdl_dims& d, int mode, int k);
 int decode_launch(const fdl_dims& d, const fdl_decode_args& g, void* ws, hipStream_t st);

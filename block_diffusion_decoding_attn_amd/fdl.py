@@ -26,7 +26,8 @@ EXPORTS = (
     "fdl_version", "fdl_strerror", "fdl_dims_check", "fdl_block_attn_workspace_size", "fdl_block_attn",
     "fdl_prefill_attn",
     "fdl_lm_head", "fdl_conf_select_workspace_size", "fdl_conf_select", "fdl_lm_head_select_workspace_size",
-    "fdl_lm_head_select", "fdl_kv_append", "fdl_decode_workspace_size", "fdl_decode_step_slots", "fdl_decode",
+    "fdl_lm_head_select", "fdl_kv_append", "fdl_kv_write", "fdl_decode_workspace_size", "fdl_decode_step_slots",
+    "fdl_decode",
 )
 
 
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
             L.fdl_lm_head_select.argtypes = [_D, _I, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_size_t, _P]
             L.fdl_kv_append.argtypes = [_D, _P, _P, _P, _P, _I, _P, _P]
+            L.fdl_kv_write.argtypes = [_D, _P, _P, _P, _P, _I, _I, _P, _P]
             L.fdl_decode_workspace_size.restype = ctypes.c_size_t
             L.fdl_decode_workspace_size.argtypes = [_D]
             L.fdl_decode_step_slots.restype = ctypes.c_int32
@@ -287,6 +289,22 @@ def fdl_kv_append(dims: fdl_dims, k_cache, v_cache, k_new, v_new, length, stream
     rc = lib().fdl_kv_append(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), n_new,
                              _ptr(length), _stream(stream))
     _check("fdl_kv_append", rc)
+
+
+def fdl_kv_write(dims: fdl_dims, k_cache, v_cache, k_new, v_new, pos: int, length=None, stream=None):
+    d = dims
+    dt = _dtype(d)
+    cap = d.prompt_len + d.gen_len
+    n_new = k_new.shape[2]
+    _expect("k_cache", k_cache, (d.batch, d.n_kv_heads, cap, d.head_dim), dt)
+    _expect("v_cache", v_cache, (d.batch, d.n_kv_heads, cap, d.head_dim), dt)
+    _expect("k_new", k_new, (d.batch, d.n_kv_heads, n_new, d.head_dim), dt)
+    _expect("v_new", v_new, (d.batch, d.n_kv_heads, n_new, d.head_dim), dt)
+    if length is not None:
+        _expect("len", length, (d.batch,), torch.int32)
+    rc = lib().fdl_kv_write(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), pos, n_new,
+                            _ptr(length), _stream(stream))
+    _check("fdl_kv_write", rc)
 
 
 def fdl_decode_workspace_size(dims: fdl_dims) -> int:

@@ -60,9 +60,16 @@ class StepRunner:
         kc, vc = synth.kv_cache(cfg, seed, fill=None if self.dual else fill)
         self.kc_host, self.vc_host = (kc, vc) if keep_host else (None, None)
         self.k_cache, self.v_cache = kc.to(self.dev), vc.to(self.dev)
-        self.len = torch.full((B,), fill, dtype=torch.int32, device=self.dev)
-
+        # per-sequence lengths and the masked rows of every step share one byte
+        # buffer, so that reset() is a single copy: [len: B int32, padded to
+        # 16 bytes][masked: steps x B x S]
         self.step_ids = list(range(len(self.sched))) if steps is None else list(steps)
+        n_steps = len(self.step_ids)
+        len_bytes = (4 * B + 15) // 16 * 16
+        self.state = torch.zeros((len_bytes + n_steps * B * S,), dtype=torch.uint8, device=self.dev)
+        self.len = self.state[:4 * B].view(torch.int32)
+        self.len.fill_(fill)
+
         self.blocks = sorted({self.sched[i][0] for i in self.step_ids})
         self.kb_host: Dict[int, tuple] = {}
         self.k_blk: Dict[int, torch.Tensor] = {}
@@ -81,8 +88,9 @@ class StepRunner:
         # masked state of every step: the select updates it in place (committed
         # rows leave the masked set); reset() restores the initial state
         masks = [synth.masked_rows(cfg, i, seed) for i in self.step_ids]
-        self.masked_init = torch.stack(masks).to(self.dev)
-        self.masked_all = self.masked_init.clone()
+        self.masked_all = self.state[len_bytes:].view(n_steps, B, S)
+        self.masked_all.copy_(torch.stack(masks))
+        self.state_init = self.state.clone()
         for n, i in enumerate(self.step_ids):
             b, s, app = self.sched[i]
             q = synth.queries(cfg, i, seed)
@@ -112,14 +120,12 @@ class StepRunner:
     def reset(self):
         """Back to the start of the schedule: the cache holds only the prompt and
         every step's rows are masked as initially drawn."""
-        self.len.fill_(self.cfg.prompt_len)
-        self.masked_all.copy_(self.masked_init)
+        self.state.copy_(self.state_init)
 
     def refresh_block(self, b: int):
-        """v1 DualCache refresh before block b: len = 0, rewrite all P + L positions."""
+        """v1 DualCache refresh before block b: rewrite all P + L positions, len = P + L."""
         kr, vr, _ = self.refresh[b]
-        self.len.zero_()
-        fdl.fdl_kv_append(self.dims, self.k_cache, self.v_cache, kr, vr, self.len)
+        fdl.fdl_kv_write(self.dims, self.k_cache, self.v_cache, kr, vr, 0, self.len)
 
     def attention(self, i: int):
         inp = self.inputs[i]

@@ -239,6 +239,18 @@ int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x
 int fdl_kv_append(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new,
                   const void* v_new, int32_t n_new, int32_t* len, void* stream);
 
+/* KV write at a caller-given position, the same for every sequence: the
+ * refresh of the v1 caches ("Fast-dLLM: Reusing Bidirectional State ...",
+ * Algorithm 1 and the DualCache of section 3) rewrites every cached position
+ * from 0, which this does in one launch without first clearing len.
+ *   k_cache, v_cache [B][Hkv][P+L][d] (dtype), written at [pos, pos + n_new)
+ *   k_new, v_new     [B][Hkv][n_new][d] (dtype)
+ *   pos, n_new       0 <= pos, 1 <= n_new, pos + n_new <= P + L (else FDL_E_INVAL)
+ *   len              [B] int32 set to pos + n_new, or NULL to leave lengths alone
+ * Bitwise copy; nothing is read from len. */
+int fdl_kv_write(const fdl_dims* dims, void* k_cache, void* v_cache, const void* k_new,
+                 const void* v_new, int32_t pos, int32_t n_new, int32_t* len, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Decode loop: a whole generation of a batch, with every control decision
  * taken on the device.

@@ -308,6 +308,18 @@ def commit_update(tokens, masked, token, commit):
 # KV append  ([v2] Level 3 block-level cache; [v1] Algorithm 1 refresh)
 # ----------------------------------------------------------------------------
 
+def kv_write(cache, new, pos):
+    """[v1] Algorithm 1 refresh: write new[B][Hkv][n][d] into every sequence's
+    cache at positions pos .. pos+n-1; the lengths become pos + n.  Returns
+    copies."""
+    cache = np.array(cache, copy=True)
+    n = new.shape[2]
+    if pos < 0 or pos + n > cache.shape[2]:
+        raise ValueError("write outside the cache")
+    cache[:, :, pos:pos + n] = new
+    return cache, np.full(cache.shape[0], pos + n, dtype=np.int64)
+
+
 def kv_append(cache, new, length):
     """Write new[B][Hkv][n][d] into cache[B][Hkv][cap][d] at positions
     length[b] .. length[b]+n-1 and advance length[b] by n.  Returns copies."""

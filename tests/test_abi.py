@@ -114,6 +114,12 @@ def test_entry_points_reject_before_launch(L):
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 0, fake, None) == -1
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 1537, fake, None) == -1
     assert L.fdl_kv_append(by(d), fake, fake, fake, fake, 32, None, None) == -1
+    # write at a position: inside the cache, with a block to write
+    assert L.fdl_kv_write(by(d), fake, fake, fake, fake, -1, 32, fake, None) == -1
+    assert L.fdl_kv_write(by(d), fake, fake, fake, fake, 1536 - 31, 32, fake, None) == -1
+    assert L.fdl_kv_write(by(d), fake, fake, fake, fake, 0, 0, fake, None) == -1
+    assert L.fdl_kv_write(by(d), fake, None, fake, fake, 0, 32, fake, None) == -1
+    assert L.fdl_kv_write(None, fake, fake, fake, fake, 0, 32, None, None) == -1
 
 
 def test_workspace_too_small_rejected(L):

@@ -241,6 +241,30 @@ def test_kv_append_bitwise(kw, lens, n_new):
         assert lg.tolist() == ok_l.tolist()
 
 
+@pytest.mark.parametrize("kw,pos,n_new,with_len", [
+    (dict(), 0, 128, True),                                                  # refresh: every position from 0
+    (dict(), 64, 32, True),                                                  # one block at a position
+    (dict(dtype="bf16", n_kv_heads=4, head_dim=128, prompt_len=100, gen_len=64, batch=3), 131, 33, False),
+    (dict(dtype="bf16", n_kv_heads=1, head_dim=64, prompt_len=0, gen_len=32, batch=2), 0, 32, True),
+])
+def test_kv_write_bitwise(kw, pos, n_new, with_len):
+    cfg = dataclasses.replace(synth.get_config("tiny_fp32"), **kw)
+    dev = _dev()
+    d = fdl.make_dims(cfg)
+    kc, vc = synth.kv_cache(cfg, 0)
+    kn = synth.normal((cfg.batch, cfg.n_kv_heads, n_new, cfg.head_dim), 0, cfg.cfg_id, 42, dtype=cfg.torch_dtype)
+    vn = synth.normal((cfg.batch, cfg.n_kv_heads, n_new, cfg.head_dim), 0, cfg.cfg_id, 43, dtype=cfg.torch_dtype)
+    lnd = torch.full((cfg.batch,), -7, dtype=torch.int32, device=dev)
+    kcd, vcd = kc.to(dev), vc.to(dev)
+    fdl.fdl_kv_write(d, kcd, vcd, kn.to(dev), vn.to(dev), pos, lnd if with_len else None)
+    torch.cuda.synchronize()
+    bits = torch.int16 if cfg.torch_dtype == torch.bfloat16 else torch.int32
+    for got, cache, new in ((kcd, kc, kn), (vcd, vc, vn)):
+        ref, ref_len = O.kv_write(cache.view(bits).numpy(), new.view(bits).numpy(), pos)
+        np.testing.assert_array_equal(got.cpu().view(bits).numpy(), ref)
+    assert lnd.cpu().tolist() == (ref_len.tolist() if with_len else [-7] * cfg.batch)
+
+
 @pytest.mark.parametrize("B,R,H,V,dtype,mode", [
     (4, 8, 512, 1000, "bf16", O.SELECT_THRESHOLD),      # V not a multiple of the 128-row tile
     (1, 8, 256, 4096, "bf16", O.SELECT_TOPK),

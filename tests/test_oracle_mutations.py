@@ -110,6 +110,19 @@ def _m_append_shift(cache, new, length):
     return cache, length2
 
 
+_orig_write = O.kv_write
+
+
+def _m_write_keeps_length(cache, new, pos):
+    c, ln = _orig_write(cache, new, pos)
+    return c, ln - new.shape[2]
+
+
+def _m_write_one_late(cache, new, pos):
+    c, ln = _orig_write(cache, new, pos)
+    return np.roll(c, 1, axis=2), ln
+
+
 def _m_lm_head_transposed(x, w):
     return O._f64(x) @ O._f64(w)
 
@@ -194,6 +207,8 @@ MUTATIONS = [
     ("argmax tie to the highest id", "row_confidence", _m_last_argmax),
     ("confidence excludes the top token from the partition", "row_confidence", _m_conf_logit),
     ("append written one position late", "kv_append", _m_append_shift),
+    ("write leaves the lengths at pos", "kv_write", _m_write_keeps_length),
+    ("write one position late", "kv_write", _m_write_one_late),
     ("LM head with untransposed W", "lm_head", _m_lm_head_transposed),
     ("factor rule <= instead of <", "select_rows", _m_factor_le),
     ("threshold rule without fallback", "select_rows", _m_no_fallback),

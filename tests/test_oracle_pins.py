@@ -414,6 +414,30 @@ def test_c8_append_reproduces_concatenation():
         O.kv_append(cache, r.standard_normal((B, Hkv, 8, d)), ln)
 
 
+def test_kv_write_refresh_and_append_agree():
+    """[v1] Algorithm 1 refresh: writing all P + L positions from 0 leaves
+    exactly the new K/V and lengths P + L; a write at the common length of
+    every sequence is the append of the same block."""
+    r = rng(33)
+    B, Hkv, cap, d = 3, 2, 24, 4
+    cache = r.standard_normal((B, Hkv, cap, d))
+    full = r.standard_normal((B, Hkv, cap, d))
+    c2, ln = O.kv_write(cache, full, 0)
+    np.testing.assert_array_equal(c2, full)
+    assert ln.tolist() == [cap] * B
+    blk = r.standard_normal((B, Hkv, 8, d))
+    cw, lw = O.kv_write(cache, blk, 8)
+    ca, la = O.kv_append(cache, blk, np.full(B, 8))
+    np.testing.assert_array_equal(cw, ca)
+    assert lw.tolist() == la.tolist() == [16] * B
+    np.testing.assert_array_equal(cw[:, :, :8], cache[:, :, :8])
+    np.testing.assert_array_equal(cw[:, :, 16:], cache[:, :, 16:])
+    with pytest.raises(ValueError):
+        O.kv_write(cache, blk, cap - 7)
+    with pytest.raises(ValueError):
+        O.kv_write(cache, blk, -1)
+
+
 # ----------------------------------------------------------------------------
 # prefill / refresh attention (multi-block queries)
 # ----------------------------------------------------------------------------
