@@ -149,8 +149,12 @@ class StepRunner:
                                inp.masked, self.ws_sel)
 
     def append(self, i: int):
+        """Store the finished block b.  The batch moves in lock-step (every
+        sequence's block b starts at P + b*D), so the position is known here
+        and the write needs no device-side length: one launch."""
         b = self.inputs[i].block_idx
-        fdl.fdl_kv_append(self.dims, self.k_cache, self.v_cache, self.k_blk[b], self.v_blk[b], self.len)
+        fdl.fdl_kv_write(self.dims, self.k_cache, self.v_cache, self.k_blk[b], self.v_blk[b],
+                         self.cfg.prompt_len + b * self.cfg.block, self.len)
 
     def step(self, i: int):
         inp = self.inputs[i]
