@@ -10,9 +10,11 @@
  *   fdl_conf_select  greedy token, confidence, commit set per sequence
  *   fdl_kv_append    append a finished block's K/V to the cache
  * fdl_lm_head_select runs the second and third as one pass that never
- * materializes the logits.  fdl_prefill_attn is the multi-block attention of
- * the prompt prefill and of the v1 cache refresh; fdl_decode runs a whole
- * generation (steps, sub-blocks, blocks, EOS) with its control on the device.
+ * materializes the logits.  fdl_kv_write stores K/V at a position the caller
+ * knows (the v1 refresh from position 0, or a lock-step batch's block) in one
+ * launch.  fdl_prefill_attn is the multi-block attention of the prompt
+ * prefill and of the v1 cache refresh; fdl_decode runs a whole generation
+ * (steps, sub-blocks, blocks, EOS) with its control on the device.
  *
  * Pages defining the operations (cited by title and section):
  *   "Fast-dLLM v2: Efficient Block-Diffusion LLM" (technical breakdown):
