@@ -748,23 +748,23 @@ static AttnPlan plan_for(const fdl_dims& d, int lk) {
   const int tiles = (lk + TK - 1) / TK;
   const int target_wg = 256;                       // one workgroup per CU
   int want = (target_wg + pairs - 1) / pairs;
-  int tiles_per_split = (tiles + want - 1) / want;
-  if (tiles_per_split < 2) tiles_per_split = 2;    // amortize the partial write
+  // as many splits as fill the chip, down to one tile each: with few KV heads
+  // (1.5B/bs1: 2) the splits' tiles are the only parallelism there is
+  const int tiles_per_split = (tiles + want - 1) / want;
   p.split_keys = tiles_per_split * TK;
   p.nsplit = (lk + p.split_keys - 1) / p.split_keys;
   return p;
 }
 
 // Largest split count any call with these dims can use: plan_for gives
-// nsplit = ceil(tiles / tiles_per_split) with tiles_per_split >= max(2,
-// ceil(tiles / want)), so nsplit <= min(want, ceil(tiles / 2)) for every key
-// count up to the capacity.
+// nsplit = ceil(tiles / tiles_per_split) with tiles_per_split =
+// ceil(tiles / want), so nsplit <= min(want, tiles) for every key count up to
+// the capacity.
 static int max_splits(const fdl_dims& d) {
   const int pairs = d.batch * d.n_kv_heads;
   const int want = (256 + pairs - 1) / pairs;
   const int tiles = (d.prompt_len + d.gen_len + TK - 1) / TK;
-  const int n = (tiles + 1) / 2;
-  return n < want ? n : want;
+  return tiles < want ? tiles : want;
 }
 
 size_t attn_workspace_bytes(const fdl_dims& d) {
