@@ -208,6 +208,36 @@ __global__ __launch_bounds__(FIN_NT) void select_finalize_kernel(SelArgs a) {
   }
 }
 
+// The selection rule over one sequence's rows in one wave, lane q = row q
+// (R <= 64), from every row's confidence and candidate flag in LDS: rank
+// among candidates by decreasing confidence, lower row first on ties; then
+// the threshold with the single-most-confident fallback, the fixed count, or
+// the factor rule -- the decisions of select_finalize_kernel.  Every lane of
+// the wave takes part (ballots); lanes q >= R return false.
+__device__ __forceinline__ bool wave_rule(const SelArgs& a, int q, bool live, bool cand, float conf, float tau,
+                                          const float* conf_s, const int* cand_s) {
+  int rank = 0;
+  if (live && cand) {
+    for (int p = 0; p < a.R; ++p) {
+      if (!cand_s[p]) continue;
+      const float cp = conf_s[p];
+      rank += (cp > conf || (cp == conf && p < q)) ? 1 : 0;
+    }
+  }
+  if (a.mode == FDL_SELECT_THRESHOLD) {
+    const bool above = live && cand && conf > tau;
+    if (__builtin_amdgcn_ballot_w64(above) != 0) return above;
+    return live && cand && rank == 0;  // fallback: the most confident candidate
+  }
+  if (a.mode == FDL_SELECT_TOPK) return live && cand && rank < a.k;
+  // FDL_SELECT_FACTOR
+  const int n = rank + 1;
+  int best = live && cand && float(n + 1) * (1.f - conf) < a.factor ? n : 0;
+  for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, kWave));
+  const int nstar = best > 0 ? best : 1;
+  return live && cand && rank < nstar;
+}
+
 // One workgroup of 1024 threads per sequence (R <= 64 rows), TPR threads per
 // row: no device-scope synchronization at all.  Wave 0 fetches the rule's
 // inputs (masked flags, tau) before the partials arrive.  Phase 1: each
@@ -309,27 +339,7 @@ __global__ __launch_bounds__(FSQ_NT) void select_finalize_seq_kernel(SelArgs a) 
     cand_s[q] = cand;
   }
   __builtin_amdgcn_wave_barrier();
-  int rank = 0;  // among candidates: decreasing confidence, lower row first on ties
-  if (live && cand) {
-    for (int p = 0; p < a.R; ++p) {
-      if (!cand_s[p]) continue;
-      const float cp = conf_s[p];
-      rank += (cp > conf || (cp == conf && p < q)) ? 1 : 0;
-    }
-  }
-  bool sel = false;
-  if (a.mode == FDL_SELECT_THRESHOLD) {
-    sel = live && cand && conf > tau;
-    if (__builtin_amdgcn_ballot_w64(sel) == 0) sel = live && cand && rank == 0;  // fallback: the most confident
-  } else if (a.mode == FDL_SELECT_TOPK) {
-    sel = live && cand && rank < a.k;
-  } else {  // FDL_SELECT_FACTOR
-    const int n = rank + 1;
-    int best = live && cand && float(n + 1) * (1.f - conf) < a.factor ? n : 0;
-    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, kWave));
-    const int nstar = best > 0 ? best : 1;
-    sel = live && cand && rank < nstar;
-  }
+  const bool sel = wave_rule(a, q, live, cand, conf, tau, conf_s, cand_s);
   const int n_sel = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sel));
   if (q == 0) a.n_commit[b] = n_sel;
   if (live) {
@@ -399,27 +409,7 @@ __global__ __launch_bounds__(kWave) void select_finalize_row_kernel(SelArgs a) {
     cand_s[q] = cand;
   }
   __builtin_amdgcn_wave_barrier();
-  int rank = 0;  // among candidates: decreasing confidence, lower row first on ties
-  if (live && cand) {
-    for (int p = 0; p < a.R; ++p) {
-      if (!cand_s[p]) continue;
-      const float cp = conf_s[p];
-      rank += (cp > conf || (cp == conf && p < q)) ? 1 : 0;
-    }
-  }
-  bool sel = false;
-  if (a.mode == FDL_SELECT_THRESHOLD) {
-    sel = live && cand && conf > tau;
-    if (__builtin_amdgcn_ballot_w64(sel) == 0) sel = live && cand && rank == 0;  // fallback: the most confident
-  } else if (a.mode == FDL_SELECT_TOPK) {
-    sel = live && cand && rank < a.k;
-  } else {  // FDL_SELECT_FACTOR
-    const int n = rank + 1;
-    int best = live && cand && float(n + 1) * (1.f - conf) < a.factor ? n : 0;
-    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, kWave));
-    const int nstar = best > 0 ? best : 1;
-    sel = live && cand && rank < nstar;
-  }
+  const bool sel = wave_rule(a, q, live, cand, conf, tau, conf_s, cand_s);
   const int n_sel = __builtin_popcountll(__builtin_amdgcn_ballot_w64(sel));
   if (q == 0) {
     a.n_commit[b] = n_sel;
