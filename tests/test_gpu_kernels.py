@@ -148,7 +148,8 @@ def _select_case(B, R, V, masked, tau, mode=O.SELECT_THRESHOLD, k=0, factor=1.0,
 # sequence (8, 16, 32 or 64 row slots: R = 8, 16, 32, 40); R > 64 the 256-thread per-row kernel
 @pytest.mark.parametrize("B,R,V", [(1, 32, 512), (4, 8, 152064), (3, 8, 1003), (2, 256, 4096), (16, 32, 2048),
                                    (1, 1, 2), (5, 3, 100000), (9, 8, 5000), (3, 24, 3001),
-                                   (40, 8, 3000), (20, 16, 2000), (9, 40, 777)])
+                                   (40, 8, 3000), (20, 16, 2000), (9, 40, 777),
+                                   (300, 1, 2000), (32, 8, 1500)])   # one row per sequence; exactly 256 rows
 @pytest.mark.parametrize("mode", [O.SELECT_THRESHOLD, O.SELECT_TOPK, O.SELECT_FACTOR])
 def test_conf_select_parity(B, R, V, mode):
     rng = np.random.default_rng(B * 1000 + R + V)
