@@ -36,7 +36,9 @@ HBM_PEAK_GBS = 8000.0
 # ~5 us of GPU time per step (2.8% of the 7B/bs4 step) for the same average.
 EV_EVERY = 8
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "lm_head_qwen2.5-7b_bs4_pmc.txt")
+def pmc_profile(workload):
+    """Path of the committed FETCH_SIZE / WRITE_SIZE summary of a workload's LM head."""
+    return os.path.join(ROOT, "profiles", f"lm_head_{workload}_pmc.txt")
 LM_HEAD_SRC = os.path.join(ROOT, "block_diffusion_decoding_attn_amd", "csrc", "lm_head.hip")
 
 
@@ -76,10 +78,11 @@ def pmc_traffic(workload, per_launch_units=1):
     """HBM bytes per launch from the committed rocprofv3 counter summary, scaled
     by the copy-kernel calibration; None when missing, taken on another
     workload, or the kernel source changed since."""
-    if not os.path.exists(PROFILE_PMC):
+    path = pmc_profile(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PROFILE_PMC):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
