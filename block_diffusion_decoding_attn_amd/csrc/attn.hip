@@ -619,6 +619,13 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
   // t & 1; its load is issued two tiles ahead of its use, so two tiles of
   // MFMA work cover its latency
   const int ntiles = (k_end - k_begin + TK - 1) / TK;
+  // A wave whose row blocks are all padding (G*S rows short of the NW*32 the
+  // workgroup covers) only helps stage the tiles: its scores would never be
+  // stored (2-3% off the attention at 56 and 32 rows per KV head).
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: a scalar branch
+  bool wave_live = false;
+#pragma unroll
+  for (int j = 0; j < RB; ++j) wave_live |= row0 + (wave_s + NW * j) * 32 < rows;
   load_tile(0, k_begin);
   if (ntiles > 1) load_tile(1, k_begin + TK);
   store_tile(0, 0);
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
   // indexed at run time without going to scratch), hence the loop by two
   auto step = [&](int t, int buf) {
     if (t + 2 < ntiles) load_tile(buf, k_begin + (t + 2) * TK);  // stage buf held tile t, already in LDS
-    compute_tile(buf, k_begin + t * TK);
+    if (wave_live) compute_tile(buf, k_begin + t * TK);
     if (t + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
     __syncthreads();
   };
