@@ -377,8 +377,12 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
 // cross-lane exchange (lane ^ 32).  The running maximum is only moved when a
 // tile raises it by more than 2^8 (log2 units 8): p then stays below 256, the
 // normalization is unchanged, and the O/l rescale is skipped on most tiles.
+// Registers are held to 256 per lane (two waves per SIMD) also for the 4-wave
+// form: left to itself the compiler spreads that form over 332 and the copies
+// between the two register files cost 5-7% (same results bit for bit).
 template <int DH, int NW>
-__global__ __launch_bounds__(NW * 64) void block_attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void block_attn_bf16_kernel(
+    AttnArgs a) {
   if (gate_closed(a.gate)) return;
   constexpr int RB = 1;
   constexpr int KSTEPS = DH / 16, DT = DH / 32;
