@@ -11,6 +11,17 @@ workload is the Qwen2.5-7B-shaped one (batch 4, 28/4 heads, d 128, prompt
 schedule is replayed until K steps have been timed.  Inputs are resident in
 HBM before timing starts.  Prints one JSON line.
 
+Two kernels carry a roofline entry: the LM head + select call (`roofline`,
+the step's dominant launch) and the block attention (`roofline_attention`);
+each is bracketed by HIP events on every EV_EVERY-th timed step, on the stream
+it is launched on.
+
+    python bench.py --calibrate-counters [MiB]
+
+runs only a plain device copy of a known size, for rocprofv3 --pmc runs that
+calibrate the FETCH_SIZE / WRITE_SIZE counters (what they report for a copy
+that moves exactly that many bytes each way).
+
 With --decode-loop a timed unit is instead one whole generation of the batch
 through fdl_decode (the device-side decode loop with its stand-in model):
 every block, sub-block and step until all positions are committed or EOS
@@ -36,10 +47,15 @@ HBM_PEAK_GBS = 8000.0
 # ~5 us of GPU time per step (2.8% of the 7B/bs4 step) for the same average.
 EV_EVERY = 8
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-def pmc_profile(workload):
-    """Path of the committed FETCH_SIZE / WRITE_SIZE summary of a workload's LM head."""
-    return os.path.join(ROOT, "profiles", f"lm_head_{workload}_pmc.txt")
-LM_HEAD_SRC = os.path.join(ROOT, "block_diffusion_decoding_attn_amd", "csrc", "lm_head.hip")
+CSRC = os.path.join(ROOT, "block_diffusion_decoding_attn_amd", "csrc")
+LM_HEAD_SRC = os.path.join(CSRC, "lm_head.hip")
+ATTN_SRC = os.path.join(CSRC, "attn.hip")
+
+
+def pmc_profile(workload, kernel="lm_head"):
+    """Path of the committed FETCH_SIZE / WRITE_SIZE summary of a workload's
+    LM head ("lm_head") or block attention ("attn")."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
 
 
 def lm_head_bytes_flops(cfg, fused: bool):
@@ -74,11 +90,13 @@ def finalize_kernel_name(cfg):
     return "select_finalize_row_kernel" if rows <= 256 else "select_finalize_seq_kernel"
 
 
-def pmc_traffic(workload, per_launch_units=1):
+def pmc_traffic(workload, kernel="lm_head", per_launch_units=1):
     """HBM bytes per launch from the committed rocprofv3 counter summary, scaled
     by the copy-kernel calibration; None when missing, taken on another
-    workload, or the kernel source changed since."""
-    path = pmc_profile(workload)
+    workload, or the kernel source changed since.  For the attention the
+    summary's figure covers the attention kernel and its split merge."""
+    path = pmc_profile(workload, kernel)
+    src = LM_HEAD_SRC if kernel == "lm_head" else ATTN_SRC
     if not os.path.exists(path):
         return None
     kv = {}
@@ -87,7 +105,7 @@ def pmc_traffic(workload, per_launch_units=1):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        sha = hashlib.sha256(open(LM_HEAD_SRC, "rb").read()).hexdigest()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if kv.get("source_sha256") != sha or kv.get("workload") != workload:
             return None
         fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_scale"])
@@ -97,40 +115,129 @@ def pmc_traffic(workload, per_launch_units=1):
         return None
 
 
-def cpu_baseline(run, budget_s: float):
-    """The oracle, as it stands, on the same workload's first steps (bounded)."""
-    import numpy as np
-    from oracle import fdl_oracle as O
+def host_cores():
+    """Cores this process may run on (its CPU affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
+        return 1
+
+
+def _oracle_steps(run, steps, kc, vc, length, stage):
+    """Run the oracle over `steps` (schedule indices, in order) from the cache
+    state (kc, vc, length); add each stage's seconds to `stage`.  Returns
+    (kc, vc, length, commits, rows above tau, candidate rows)."""
+    import numpy as np
+    from oracle import fdl_oracle as O
     cfg = run.cfg
+    commits = above = cands = 0
+    for i in steps:
+        inp = run.host_inputs[i]
+        kb, vb = run.kb_host[inp.block_idx]
+        t = time.perf_counter()
+        O.block_attention(inp.q, kc, vc, kb, vb, length, mode=cfg.attn_mode, total_len=cfg.cap)
+        t1 = time.perf_counter()
+        logits = O.lm_head(inp.x, run.w_host)
+        t2 = time.perf_counter()
+        masked = inp.masked.numpy()
+        tau = inp.tau.numpy()
+        res = O.conf_select(logits.reshape(cfg.batch, cfg.sub_block, cfg.vocab), masked, tau)
+        t3 = time.perf_counter()
+        commits += int(res["n_commit"].sum())
+        above += int(((res["conf"] > tau[:, None]) & (masked > 0)).sum())
+        cands += int((masked > 0).sum())
+        if inp.append_after and cfg.attn_mode != "dual_cache":
+            kc, _ = O.kv_append(kc, kb.float().numpy(), length)
+            vc, length = O.kv_append(vc, vb.float().numpy(), length)
+        t4 = time.perf_counter()
+        for key, dt in (("attention", t1 - t), ("lm_head", t2 - t1), ("select", t3 - t2), ("append", t4 - t3)):
+            stage[key] += dt
+    return kc, vc, length, commits, above, cands
+
+
+def cpu_baseline(run, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    The sample is the steps of the schedule's first block and of its last
+    block (the cache grown by the appends of every block in between, which
+    the oracle performs untimed), each stage timed on its own (the eq 15
+    decomposition of the Fast-dLLM review, section 7: attention, LM head,
+    select, append); the first block's steps are then re-run on one thread.
+    Steps stop early once `budget_s` seconds have gone by."""
+    import numpy as np
+    from oracle import fdl_oracle as O
+    cfg = run.cfg
+    cores = host_cores()
+    threads = blas_threads()
     kc = run.kc_host.float().numpy().copy()
     vc = run.vc_host.float().numpy().copy()
     length = np.full(cfg.batch, cfg.prompt_len)
+    blocks = sorted({run.host_inputs[i].block_idx for i in run.step_ids})
+    first = [i for i in run.step_ids if run.host_inputs[i].block_idx == blocks[0]]
+    last = [i for i in run.step_ids if run.host_inputs[i].block_idx == blocks[-1]] if len(blocks) > 1 else []
+    stage = dict(attention=0.0, lm_head=0.0, select=0.0, append=0.0)
+    n = commits = above = cands = 0
     t0 = time.perf_counter()
-    n = 0
-    commits = 0
-    for i in run.step_ids:
-        inp = run.host_inputs[i]
-        kb, vb = run.kb_host[inp.block_idx]
-        O.block_attention(inp.q, kc, vc, kb, vb, length, mode=cfg.attn_mode, total_len=cfg.cap)
-        logits = O.lm_head(inp.x, run.w_host)
-        res = O.conf_select(logits.reshape(cfg.batch, cfg.sub_block, cfg.vocab), inp.masked.numpy(),
-                            inp.tau.numpy())
-        commits += int(res["n_commit"].sum())
-        if inp.append_after:
-            kc, _ = O.kv_append(kc, kb.float().numpy(), length)
-            vc, length = O.kv_append(vc, vb.float().numpy(), length)
-        n += 1
+    for i in first:
+        kc, vc, length, c, a, m = _oracle_steps(run, [i], kc, vc, length, stage)
+        n, commits, above, cands = n + 1, commits + c, above + a, cands + m
         if time.perf_counter() - t0 > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} steps of the {cfg.name} schedule (fp64 numpy oracle: attention, LM head, "
-                      f"select, append), {dt:.1f} s; {commits / dt:.3f} committed tokens/s"}
+    if last and time.perf_counter() - t0 <= budget_s and cfg.attn_mode != "dual_cache":
+        # the cache of the last block: every earlier block appended (untimed)
+        kc = run.kc_host.float().numpy().copy()
+        vc = run.vc_host.float().numpy().copy()
+        length = np.full(cfg.batch, cfg.prompt_len)
+        for b in range(blocks[-1]):
+            kb, vb = run.kb_host[b] if b in run.kb_host else (None, None)
+            if kb is None:
+                from block_diffusion_decoding_attn_amd import synth
+                kb, vb = synth.block_kv(cfg, b, run.seed)
+            kc, _ = O.kv_append(kc, kb.float().numpy(), length)
+            vc, length = O.kv_append(vc, vb.float().numpy(), length)
+    if last and time.perf_counter() - t0 <= budget_s:
+        for i in last:
+            kc, vc, length, c, a, m = _oracle_steps(run, [i], kc, vc, length, stage)
+            n, commits, above, cands = n + 1, commits + c, above + a, cands + m
+            if time.perf_counter() - t0 > budget_s:
+                break
+    busy = sum(stage.values())
+    # one thread, the first block's steps again (bounded by a third of the budget)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        kc1 = run.kc_host.float().numpy().copy()
+        vc1 = run.vc_host.float().numpy().copy()
+        len1 = np.full(cfg.batch, cfg.prompt_len)
+        st1 = dict(attention=0.0, lm_head=0.0, select=0.0, append=0.0)
+        n1 = 0
+        t1 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            for i in first:
+                kc1, vc1, len1, _, _, _ = _oracle_steps(run, [i], kc1, vc1, len1, st1)
+                n1 += 1
+                if time.perf_counter() - t1 > budget_s / 3:
+                    break
+        one = {"value": n1 / sum(st1.values()), "steps": n1}
+    except Exception:  # noqa: BLE001
+        one = None
+    sample = (f"{n} steps of the {cfg.name} schedule (blocks {blocks[0]} and {blocks[-1]}, the first and last: "
+              f"fp64 numpy oracle of attention, LM head, select, append), {busy:.1f} s; "
+              f"{commits / busy:.3f} committed tokens/s")
+    return {"value": n / busy, "unit": "steps/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "blas_threads": threads,
+            "stage_seconds_per_step": {k: v / max(n, 1) for k, v in stage.items()},
+            "committed_tokens_per_s": commits / busy,
+            "exceed_tau_fraction": above / max(cands, 1),
+            "one_thread": one}
 
 
 def attn_bytes(cfg, lk: int) -> int:
@@ -215,6 +322,47 @@ def bench_decode_loop(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def calibrate_counters(mib: int, reps: int = 4):
+    """A plain device copy that moves exactly `mib` MiB each way, `reps` times:
+    under rocprofv3 --pmc FETCH_SIZE (or WRITE_SIZE) it gives the factor
+    between what the counter reports and the bytes actually moved."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB x {reps}", flush=True)
+
+
+def exceed_tau(run, cfg, other_boost: str, n_steps: int = 8):
+    """Fraction of candidate rows whose confidence clears their tau, for the
+    run's own boost generator (its whole schedule, from the commit-counting
+    pass) and for the other one (the first n_steps steps, through
+    fdl_lm_head_select on separate buffers)."""
+    import torch
+    from block_diffusion_decoding_attn_amd import fdl, synth
+    dev = run.dev
+    B, S = cfg.batch, cfg.sub_block
+    above = cands = 0
+    for i in run.step_ids[:n_steps]:
+        x, _, _ = synth.hidden_rows(cfg, run.w_host, i, run.seed, other_boost)
+        masked = synth.masked_rows(cfg, i, run.seed).to(dev)
+        m0 = masked.clone()
+        tau = synth.taus(cfg, i, run.seed).to(dev)
+        conf = torch.empty((B, S), dtype=torch.float32, device=dev)
+        outs = [torch.empty((B, S), dtype=torch.int32, device=dev), conf,
+                torch.empty((B, S), dtype=torch.uint8, device=dev), torch.empty((B,), dtype=torch.int32, device=dev)]
+        fdl.fdl_lm_head_select(run.dims, S, x.to(dev), run.w, None, masked, tau, fdl.FDL_SELECT_THRESHOLD, 0, 1.0,
+                               *outs, None, None, run.ws_sel)
+        torch.cuda.synchronize()
+        sel = m0.bool()
+        above += int(((conf > tau[:, None]) & sel).sum())
+        cands += int(sel.sum())
+    return above / max(cands, 1), n_steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,7 +380,12 @@ def main():
                     help="time whole generations through fdl_decode instead of single steps")
     ap.add_argument("--graph", action="store_true",
                     help="with --decode-loop: capture the generation in a HIP graph and time its replays")
+    ap.add_argument("--calibrate-counters", type=int, nargs="?", const=1024, default=None, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 4 times (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_counters is not None:
+        calibrate_counters(args.calibrate_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the batch dimension would shard across GPUs with no exchange)", file=sys.stderr)
@@ -256,15 +409,24 @@ def main():
     print(f"# setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     nsched = len(run.step_ids)
 
-    # commits per schedule step (deterministic: the same inputs every pass)
+    # commits per schedule step (deterministic: the same inputs every pass),
+    # and the rows whose confidence clears tau
     run.reset()
     commits = []
+    above = cands = 0
     for i in run.step_ids:
+        m0 = run.inputs[i].masked.clone().bool()
         run.step(i)
         commits.append(int(run.n_commit.sum()))
+        above += int(((run.conf > run.inputs[i].tau[:, None]) & m0).sum())
+        cands += int(m0.sum())
     torch.cuda.synchronize()
 
-    def do_steps(n, start, ev=None):
+    # HIP events on the launch stream (torch's current stream, which the
+    # binding passes to every call): the LM head + select call on steps
+    # j % EV_EVERY == 0, the attention (kernel + split merge) on steps
+    # j % EV_EVERY == EV_EVERY // 2
+    def do_steps(n, start, ev=None, ev_attn=None):
         pos = start
         for j in range(n):
             if pos == 0:
@@ -273,7 +435,13 @@ def main():
             inp = run.inputs[i]
             if run.dual and inp.sub_idx == 0:
                 run.refresh_block(inp.block_idx)
+            t_attn = ev_attn is not None and j % EV_EVERY == EV_EVERY // 2
+            if t_attn:
+                ev_attn[j // EV_EVERY][0].record()
             run.attention(i)
+            if t_attn:
+                ev_attn[j // EV_EVERY][1].record()
+                ev_attn[j // EV_EVERY][2] = i
             timed = ev is not None and j % EV_EVERY == 0
             if timed:
                 ev[j // EV_EVERY][0].record()
@@ -294,17 +462,26 @@ def main():
     torch.cuda.synchronize()
     n_ev = (args.steps + EV_EVERY - 1) // EV_EVERY
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    ev_attn = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), None]
+               for _ in range(n_ev)]
     start_pos = pos
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    do_steps(args.steps, start_pos, ev)
+    do_steps(args.steps, start_pos, ev, ev_attn)
     t_end.record()
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end)
     ms_per_step = ms / args.steps
     committed = sum(commits[(start_pos + j) % nsched] for j in range(args.steps))
     lm_ms = sum(a.elapsed_time(b) for a, b in ev) / n_ev
+    ev_attn = [e for e in ev_attn if e[2] is not None]
+    attn_ms = sum(a.elapsed_time(b) for a, b, _ in ev_attn) / len(ev_attn)
+    attn_b = 0
+    for _, _, i in ev_attn:
+        lp = cfg.prompt_len + run.inputs[i].block_idx * cfg.block
+        attn_b += attn_bytes(cfg, cfg.cap if run.dual else lp + cfg.block)
+    attn_b /= len(ev_attn)
 
     byts, flops = lm_head_bytes_flops(cfg, run.fused)
     ai = flops / byts
@@ -321,6 +498,16 @@ def main():
     roof["kernel_us"] = lm_ms * 1e3
     roof["kernel_calls_timed"] = n_ev
     roof["algorithmic_bytes"] = byts
+
+    # the attention: HBM-bound at every workload (arithmetic intensity 31-212
+    # flop/B, below the bf16 ridge of 312)
+    a_ach = attn_b / (attn_ms * 1e-3) / 1e9
+    roof_attn = {"bound": "hbm", "achieved": a_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": a_ach / HBM_PEAK_GBS, "traffic": pmc_traffic(cfg.name, "attn"),
+                 "kernel": "fdl_block_attn (block_attn kernel + split merge)", "kernel_us": attn_ms * 1e3,
+                 "kernel_calls_timed": len(ev_attn), "algorithmic_bytes": attn_b}
+    other = "literal" if args.boost == "calibrated" else "calibrated"
+    ex_other, n_other = exceed_tau(run, cfg, other)
 
     out = {
         "metric": METRIC,
@@ -343,6 +530,10 @@ def main():
         "committed_tokens_per_s": committed / (ms * 1e-3),
         "commits_per_step": committed / args.steps,
         "roofline": roof,
+        "roofline_attention": roof_attn,
+        "exceed_tau_fraction": {args.boost: above / max(cands, 1), other: ex_other,
+                                "note": f"candidate rows with confidence > tau: {args.boost} over the whole "
+                                        f"schedule, {other} over its first {n_other} steps"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(run, args.cpu_seconds)

@@ -11,10 +11,10 @@
 //   * One workgroup per (sequence, KV head, key split).  All G = Hq/Hkv query
 //     heads x S query rows of a KV head live in the workgroup, so every K/V
 //     byte of a split is read from HBM exactly once per step.
-//   * K/V tiles of 64 keys are staged through LDS by 16-byte coalesced loads,
-//     prefetched into registers ahead of the MFMA work (two tiles ahead for
-//     bf16, one for f32).  V is written to LDS transposed so that the P.V
-//     product reads contiguous keys.
+//   * bf16: K/V tiles of 64 keys travel HBM -> LDS by direct-to-LDS loads
+//     through a 4-stage ring (no register staging); V^T operands come from
+//     transposing LDS reads.  f32 (the tiny workload): register-staged tiles,
+//     V transposed on its way into LDS.
 //   * S^T = K Q^T and O^T = V^T P^T run on MFMA (32x32x16 bf16, or 16x16x4
 //     f32 for f32 data).  In this orientation the score accumulator of a lane
 //     is exactly the P operand of the next MFMA (same query column, the same
@@ -367,38 +367,124 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
   }
 }
 
-// bf16 data: 32x32x16 MFMA (on gfx950 twice the rate of 16x16x32).  Each of
-// the NW waves owns 32 query rows (NW*32 >= G*S); every wave helps stage the
-// K/V tiles.  S^T = K Q^T leaves a lane with 32 scores of its query column
-// (lane & 31): keys key0 + 32kt + 8(v/4) + 4h + v%4, h = lane >> 5.  Packed
-// 16 at a time, those are exactly the B operand of O^T += V^T P^T under the
-// k permutation {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk, which the V^T
-// fragments read with the same permutation.  Row statistics need one
-// cross-lane exchange (lane ^ 32).  The running maximum is only moved when a
-// tile raises it by more than 2^8 (log2 units 8): p then stays below 256, the
-// normalization is unchanged, and the O/l rescale is skipped on most tiles.
-// Registers are held to 256 per lane (two waves per SIMD) also for the 4-wave
-// form: left to itself the compiler spreads that form over 332 and the copies
-// between the two register files cost 5-7% (same results bit for bit).
+// ---------------------------------------------------------------------------
+// bf16 data (every bf16 workload)
+//
+// One workgroup per (sequence, KV head, key split); wave w owns query rows
+// [32w, 32w + 32) of the KV head's G*S rows on 32x32x16 MFMA (a wave whose
+// rows are all padding only helps load).
+//
+// K/V travel HBM -> LDS by global_load_lds_dwordx4 (no register staging)
+// through a ring of NST stages of one 64-key tile each (K tile, then V tile,
+// rows of d bf16 stored as they are in memory): up to NST - 1 tiles are in
+// flight while one is consumed, with one s_waitcnt + barrier per tile.  A
+// 1 KB load instruction fills 1024 / (2d) whole key rows; lane l fetches
+// physical 16-byte chunk l % (2d / 16) of its row, which holds the logical
+// chunk named by the row's swizzle, so that both kinds of fragment reads
+// below are free of LDS bank conflicts.
+//
+// S^T = K Q^T leaves a lane with 32 scores of its query column (lane & 31):
+// keys key0 + 32kt + 8(v/4) + 4h + v%4, h = lane >> 5.  Packed 16 at a time
+// they are exactly the B operand of O^T += V^T P^T under the k order
+// {4h..4h+3, 8+4h..8+4h+3} of each 16-key chunk; the matching V^T operand
+// comes from two transposing LDS reads (ds_read_b64_tr_b16: within each 16
+// lanes, lane 4e + q reads four consecutive d of key k0 + e and every lane j
+// receives keys k0..k0+3 of column d0 + j), so V is never transposed in
+// registers.  Online softmax in fp32 with exp2 and log2(e)/sqrt(d) folded
+// into the scores; the running maximum moves only when a tile raises it by
+// more than 8 (log2 units), so P < 2^8 and most tiles skip the rescale.  The
+// row sum adds the bf16-rounded P that the P.V product uses (v_dot2 of each
+// packed pair with (1, 1)), per lane; the two half-waves combine at the end.
+//
+// Splits: every split writes (m, l, unnormalized O) in the lanes' own
+// register layout (coalesced, no transposition), then counts itself on its
+// KV head's device-scope counter; the split that arrives last merges all
+// splits of the head in split order (deterministic) from L2, writes the
+// output, and resets the counter to zero for the next call.  The splits of a
+// KV head are placed on one XCD (workgroups are dealt round-robin to the 8
+// XCDs; the logical id below groups them), so their partials meet in that
+// XCD's L2.
+constexpr int NST = 4;  // LDS ring stages (tiles)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane HBM -> LDS: lane l's 16 bytes land at LDS address
+// lds + 16 l (lds is wave-uniform; it goes to M0).  Issued from inline
+// assembly so that the compiler does not see an LDS write in flight: it would
+// otherwise wait for every outstanding load (vmcnt(0)) before each LDS read,
+// including the loads of later tiles into other stages.  The kernel waits for
+// its loads itself (wait_vm) before the barrier that precedes the reads.
+// Nothing else in the kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(l) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_barrier with the compiler kept from moving memory accesses across it
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// a ? x : y on pointer values (a conditional over two pointer variables
+// would select between their addresses and keep them in scratch memory)
+__device__ __forceinline__ const bf16_t* pick(bool a, const bf16_t* x, const bf16_t* y) {
+  const uintptr_t ux = reinterpret_cast<uintptr_t>(x), uy = reinterpret_cast<uintptr_t>(y);
+  return reinterpret_cast<const bf16_t*>(a ? ux : uy);
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((((N >> 4) & 3) << 14) | (0xF << 8) | (7 << 4) | (N & 15));
+}
+
+// Physical chunk = logical chunk ^ swizzle(row).  K (fragment reads: 32 rows
+// at one logical chunk) spreads consecutive rows over distinct chunks; V
+// (transposing reads: 4 consecutive rows x 4 chunks) spreads each group of
+// four rows over distinct 4-chunk groups.  d = 64: a row is half of the 64
+// banks, so rows 2m and 2m + 1 already differ in bank half.
+template <int DH>
+__device__ __forceinline__ int swz_k(int row) { return DH == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int DH>
+__device__ __forceinline__ int swz_v(int row) { return DH == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
+
+// Workspace of the bf16 kernel (nsplit > 1): partials of nsplit x KV heads x
+// NW waves, each PSLOT x 64 lanes floats, where a wave's PSLOT = d/2 + 2
+// values per lane are its O^T registers, m and l.
+__host__ __device__ constexpr int attn_pslot(int dh) { return dh / 2 + 2; }
+
 template <int DH, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void block_attn_bf16_kernel(
     AttnArgs a) {
   if (gate_closed(a.gate)) return;
-  constexpr int RB = 1;
-  constexpr int KSTEPS = DH / 16, DT = DH / 32;
   typedef bf16_t T;
-  constexpr int NT = NW * 64;
-  constexpr int EPC = 8, CPR = DH / EPC;
-  constexpr int KCH = TK * CPR, KCH_T = (KCH + NT - 1) / NT;
-  constexpr int VU = (TK / 4) * CPR, VU_T = (VU + NT - 1) / NT;
-  constexpr int KST = DH + 8;   // 272 B rows
-  constexpr int VST = TK + 4;   // 136 B rows
-  __shared__ __attribute__((aligned(16))) T Ks[2][TK * KST];
-  __shared__ __attribute__((aligned(16))) T Vt[2][DH * VST];
+  constexpr int ROWB = DH * 2;         // bytes per key row
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int KPI = 1024 / ROWB;     // key rows per 1 KB load instruction
+  constexpr int TILEB = TK * ROWB;     // one K (or V) tile
+  constexpr int STB = 2 * TILEB;       // one stage: K tile, then V tile
+  constexpr int IPH = TILEB / 1024;    // load instructions per K (or V) tile
+  constexpr int IPW = 2 * IPH / NW;    // load instructions per wave per stage
+  static_assert(2 * IPH % NW == 0, "whole load instructions per wave");
+  constexpr int KSTEPS = DH / 16, DT = DH / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // logical workgroup id: the workgroups of one XCD (hardware id % 8) take a
+  // contiguous run of ids, split fastest, so a KV head's splits share an L2
+  const int nwg = gridDim.x, hw = blockIdx.x;
+  const int xcd = hw & 7, k8 = hw >> 3, q8 = nwg >> 3, r8 = nwg & 7;
+  const int lid = xcd < r8 ? xcd * (q8 + 1) + k8 : r8 * (q8 + 1) + (xcd - r8) * q8 + k8;
+  const int split = lid % a.nsplit, pid = lid / a.nsplit;  // pid = b * Hkv + g
+  const int g = pid % a.Hkv, b = pid / a.Hkv;
 
   int lp = a.default_lp;
   if (a.prefix_len) {
@@ -409,282 +495,277 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int k_begin = split * a.split_keys;
   const int k_end = min(k_begin + a.split_keys, lk);
   const int rows = a.G * a.S;
-  constexpr int row0 = 0, rows_per_rg = NW * RB * 32;
   const size_t pair = size_t(b) * a.Hkv + g;
   const T* kc = reinterpret_cast<const T*>(a.kc) + pair * a.cap * DH;
   const T* vc = reinterpret_cast<const T*>(a.vc) + pair * a.cap * DH;
   const T* kbk = reinterpret_cast<const T*>(a.kb) + pair * a.D * DH;
   const T* vbk = reinterpret_cast<const T*>(a.vb) + pair * a.D * DH;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool wave_live = wave_s * 32 < rows;
+  const int r = wave * 32 + l32;  // this lane's query row (column of S^T)
 
-  if (k_begin >= lk) {
-    for (int r = row0 + tid; r < min(rows, row0 + rows_per_rg); r += NT) {
-      const int hq = g * a.G + r / a.S, i = r % a.S;
-      const size_t row = (size_t(b) * a.Hq + hq) * a.S + i;
-      float* ml = a.part_ml + (size_t(split) * a.B * a.Hq * a.S + row) * 2;
-      ml[0] = -INFINITY;
-      ml[1] = 0.f;
-    }
-    return;
-  }
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m = -INFINITY, l = 0.f;  // l: this lane's share of the row sum
 
-  u32x4 qf[RB][KSTEPS];
+  if (k_begin < lk) {
+    // this lane's share of the wave's load instructions.  A wave's IPW
+    // instructions all fill the K tile or all the V tile of a stage
+    // (IPH is a multiple of IPW); instruction j fills 1 KB at ld_lds[j] with
+    // key rows KPI * i .. of the tile, this lane one chunk of row ld_row[j].
+    static_assert(IPH % IPW == 0, "a wave loads only K or only V");
+    const bool wave_v = wave_s * IPW >= IPH;
+    const T* const my_cache = pick(wave_v, vc, kc);
+    const T* const my_blk = pick(wave_v, vbk, kbk);
+    int ld_row[IPW], ld_elem[IPW], ld_lds[IPW];
 #pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    const int r = row0 + (wave + NW * j) * 32 + l32;
-    const bool ok = r < rows;
-    const T* qp = nullptr;
-    if (ok) {
-      const int hq = g * a.G + r / a.S, i = r % a.S;
-      qp = reinterpret_cast<const T*>(a.q) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
+    for (int j = 0; j < IPW; ++j) {
+      const int i = wave_s * IPW + j - (wave_v ? IPH : 0);
+      const int row = KPI * i + lane / CPR;
+      const int c = (lane % CPR) ^ (wave_v ? swz_v<DH>(row) : swz_k<DH>(row));
+      ld_row[j] = row;
+      ld_elem[j] = c * 8;
+      ld_lds[j] = (wave_v ? TILEB : 0) + i * 1024;
     }
+    const int ntiles = (k_end - k_begin + TK - 1) / TK;
+    u32x4 qf[KSTEPS];  // B operand of S^T = K Q^T: query column l32, d = 16ks + 8h .. + 7
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      const int key0 = k_begin + t * TK;
+      char* sb = smem + (t % NST) * STB;
+      const bool fast = key0 + TK <= k_end && (key0 + TK <= lp || key0 >= lp + a.D);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[j][ks] = ok ? ld16(qp + ks * 16 + 8 * h) : u32x4{0, 0, 0, 0};
-  }
-  f32x16 o[RB][DT];
-  float m[RB], l[RB];
-#pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[j][dt][e] = 0.f;
-  }
-  auto key_ptr = [&](const T* cache, const T* blk, int j) -> const T* {
-    if (j >= lp && j < lp + a.D) return blk + size_t(j - lp) * DH;
-    return cache + size_t(j) * DH;
-  };
-  // two register stages: tile t + 2 is fetched while tile t is computed
-  u32x4 kreg[2][KCH_T];
-  u32x4 vreg[2][VU_T][4];
-  // Per-thread source offsets of the K and V chunks within a tile; a tile that
-  // lies wholly inside the cache (no block keys, no key past the split) takes
-  // them with a scalar offset, the rest go through the per-key selection.
-  int koff[KCH_T], voff[VU_T][4];
-#pragma unroll
-  for (int c = 0; c < KCH_T; ++c) {
-    const int ch = tid + c * NT;
-    koff[c] = (ch / CPR) * DH + (ch % CPR) * EPC;
-  }
-#pragma unroll
-  for (int u = 0; u < VU_T; ++u) {
-    const int un = tid + u * NT;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) voff[u][e] = ((un % (TK / 4)) * 4 + e) * DH + (un / (TK / 4)) * EPC;
-  }
-  auto load_tile = [&](int rs, int key0) {
-    const bool fast = key0 + TK <= k_end && (key0 + TK <= lp || key0 >= lp + a.D);
-    if (fast) {
-      const T* kt = kc + size_t(key0) * DH;
-      const T* vt = vc + size_t(key0) * DH;
-#pragma unroll
-      for (int c = 0; c < KCH_T; ++c)
-        if (KCH % NT == 0 || tid + c * NT < KCH) kreg[rs][c] = ld16(kt + koff[c]);
-#pragma unroll
-      for (int u = 0; u < VU_T; ++u)
-        if (VU % NT == 0 || tid + u * NT < VU) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vreg[rs][u][e] = ld16(vt + voff[u][e]);
+      for (int j = 0; j < IPW; ++j) {
+        size_t off;     // element offset from my_cache (or my_blk)
+        bool in_blk = false;
+        if (fast) {
+          off = size_t(key0 + ld_row[j]) * DH;
+        } else {
+          // keys past the split's end read a valid row; their scores are masked
+          const int key = min(key0 + ld_row[j], k_end - 1);
+          in_blk = key >= lp && key < lp + a.D;
+          off = size_t(in_blk ? key - lp : key) * DH;
         }
-      return;
-    }
+        const T* base = pick(in_blk, my_blk, my_cache);
+        load_lds16(base + off + ld_elem[j], sb + ld_lds[j]);
+      }
+    };
+
+    // per-lane LDS byte offsets of the fragment reads (the tile, chunk and
+    // stage parts are immediate offsets)
+    int koff[KSTEPS];
 #pragma unroll
-    for (int c = 0; c < KCH_T; ++c) {
-      const int ch = tid + c * NT;
-      kreg[rs][c] = u32x4{0, 0, 0, 0};
-      if (ch < KCH) {
-        const int key = key0 + ch / CPR;
-        if (key < k_end) kreg[rs][c] = ld16(key_ptr(kc, kbk, key) + (ch % CPR) * EPC);
+    for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + h) ^ swz_k<DH>(l32)) << 4);
+    int voff[DT];
+    {
+      const int grp = lane >> 4, sl = lane & 15, e = sl >> 2, qq = sl & 3;
+      const int row = 4 * (grp >> 1) + e;  // key row within each 16-key chunk (first read)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + 16 * (grp & 1) + 4 * qq;
+        voff[dt] = row * ROWB + (((d >> 3) ^ swz_v<DH>(row)) << 4) + (d & 7) * 2;
       }
     }
-#pragma unroll
-    for (int u = 0; u < VU_T; ++u) {
-      const int un = tid + u * NT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vreg[rs][u][e] = u32x4{0, 0, 0, 0};
-        if (un < VU) {
-          const int key = key0 + (un % (TK / 4)) * 4 + e;
-          if (key < k_end) vreg[rs][u][e] = ld16(key_ptr(vc, vbk, key) + (un / (TK / 4)) * EPC);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int rs, int buf) {
-#pragma unroll
-    for (int c = 0; c < KCH_T; ++c) {
-      const int ch = tid + c * NT;
-      if (ch < KCH) *reinterpret_cast<u32x4*>(&Ks[buf][(ch / CPR) * KST + (ch % CPR) * EPC]) = kreg[rs][c];
-    }
-#pragma unroll
-    for (int u = 0; u < VU_T; ++u) {
-      const int un = tid + u * NT;
-      if (un >= VU) continue;
-      const int k4 = (un % (TK / 4)) * 4;
-      const int d0 = (un / (TK / 4)) * EPC;
-      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][0]);
-      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][1]);
-      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][2]);
-      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&vreg[rs][u][3]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        u32x2 w;
-        w[0] = uint32_t(e0[x]) | (uint32_t(e1[x]) << 16);
-        w[1] = uint32_t(e2[x]) | (uint32_t(e3[x]) << 16);
-        *reinterpret_cast<u32x2*>(&Vt[buf][(d0 + x) * VST + k4]) = w;
-      }
-    }
-  };
-  auto compute_tile = [&](int buf, int key0) {
-    // S^T = K Q^T: s[j][kt][v] = score of key key0 + 32kt + 8(v/4) + 4h + v%4, query column l32
-    f32x16 s[RB][2];
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
+    const float c = a.scale_log2;
+
+    auto compute = [&](int t) __attribute__((always_inline)) {
+      const int key0 = k_begin + t * TK;
+      const char* Ks = smem + (t % NST) * STB;
+      const char* Vs = Ks + TILEB;
+      f32x16 s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[j][kt][e] = 0.f;
+        for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
+      for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(&Ks[buf][(kt * 32 + l32) * KST + ks * 16 + 8 * h]);
-#pragma unroll
-        for (int j = 0; j < RB; ++j) s[j][kt] = mfma32x32x16_bf16(kf, qf[j][ks], s[j][kt]);
-      }
-    }
-    const bool partial = key0 + TK > k_end;
-    const float c = a.scale_log2;
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      if (partial) {
+        for (int kt = 0; kt < 2; ++kt) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + kt * 32 * ROWB + koff[ks]);
+          s[kt] = mfma32x32x16_bf16(kf, qf[ks], s[kt]);
+        }
+      if (key0 + TK > k_end) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (key0 + kt * 32 + (v / 4) * 8 + h * 4 + (v % 4) >= k_end) s[j][kt][v] = -INFINITY;
+            if (key0 + kt * 32 + (v / 4) * 8 + h * 4 + (v % 4) >= k_end) s[kt][v] = -INFINITY;
       }
-      float mx = s[j][0][0];
+      float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[0][v]), s[0][v + 1]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][kt][v]);
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[1][v]), s[1][v + 1]);
       mx = xor32_max(mx) * c;
-      // lazy rescale: keep the running reference unless the new maximum
-      // exceeds it by more than 8 (log2 units); p then stays below 2^8
-      if (__builtin_amdgcn_ballot_w64(mx > m[j] + 8.f) != 0) {
-        const float mn = fmaxf(m[j], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[j] - mn);
-        l[j] *= alpha;
+      if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[j][dt] *= alpha;
-        m[j] = mn;
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m = mn;
       }
-      float rs = 0.f;
-      const float mneg = -m[j];
+      const float mneg = -m;
+      const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[j][kt][v], c, mneg));
-          s[j][kt][v] = p;
-          rs += p;
+        for (int q = 0; q < 2; ++q) {
+          u32x4 pf;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * q + 2 * w], c, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * q + 2 * w + 1], c, mneg));
+            // (a named value: a bit cast of the vector element pf[w] reads element 0)
+            const uint32_t pw = pack_bf16x2(p0, p1);
+            pf[w] = pw;
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, l, false);
+          }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const char* vb0 = Vs + (kt * 32 + q * 16) * ROWB + voff[dt];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vb0));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vb0 + 8 * ROWB));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 vf{lo2[0], lo2[1], hi2[0], hi2[1]};
+            o[dt] = mfma32x32x16_bf16(vf, pf, o[dt]);
+          }
         }
-      rs = xor32_sum(rs);
-      l[j] += rs;
-    }
-    // O^T += V^T P^T over 16-key chunks (kt, q)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        u32x4 pf[RB];
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          pf[j][0] = pack_bf16x2(s[j][kt][8 * q + 0], s[j][kt][8 * q + 1]);
-          pf[j][1] = pack_bf16x2(s[j][kt][8 * q + 2], s[j][kt][8 * q + 3]);
-          pf[j][2] = pack_bf16x2(s[j][kt][8 * q + 4], s[j][kt][8 * q + 5]);
-          pf[j][3] = pack_bf16x2(s[j][kt][8 * q + 6], s[j][kt][8 * q + 7]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const T* row = &Vt[buf][(dt * 32 + l32) * VST + kt * 32 + q * 16 + h * 4];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
-          const u32x4 vf{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int j = 0; j < RB; ++j) o[j][dt] = mfma32x32x16_bf16(vf, pf[j], o[j][dt]);
-        }
+    };
+
+    issue(0);
+    if (ntiles > 1) issue(1);
+    {
+      const bool ok = r < rows;
+      const T* qp = nullptr;
+      if (ok) {
+        const int hq = g * a.G + r / a.S, i = r % a.S;
+        qp = reinterpret_cast<const T*>(a.q) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
       }
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = ok ? ld16(qp + ks * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+    }
+    // the query fragments (and the first two tiles) have landed before the
+    // third tile is issued: the compiler does not count the tile loads, so
+    // it must not be left to wait for Q inside the loop
+    wait_vm<0>();
+    if (ntiles > 2) issue(2);
+    for (int t = 0; t < ntiles; ++t) {
+      // this wave's loads of tile t are done once at most those of the (up to
+      // two) later tiles already issued are in flight; after the barrier every
+      // wave's are, and every wave is done with tile t - 1, whose stage the
+      // loads of tile t + 3 then refill
+      if (t + 2 < ntiles) wait_vm<2 * IPW>();
+      else if (t + 1 < ntiles) wait_vm<IPW>();
+      else wait_vm<0>();
+      bare_barrier();
+      if (t + 3 < ntiles) issue(t + 3);
+      if (wave_live) compute(t);
+    }
+  }
+  l = xor32_sum(l);  // both half-waves' shares of the row sum
+
+  // o[dt][v] = O^T[d = 32dt + 8(v/4) + 4h + v%4][query row r]
+  auto store_out = [&](const f32x16* oo, float mm, float ll) __attribute__((always_inline)) {
+    if (r >= rows) return;
+    const int hq = g * a.G + r / a.S, i = r % a.S;
+    const float inv = 1.f / ll;
+    T* op = reinterpret_cast<T*>(a.out) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        store4(op + dt * 32 + q4 * 8 + h * 4,
+               f32x4{oo[dt][4 * q4], oo[dt][4 * q4 + 1], oo[dt][4 * q4 + 2], oo[dt][4 * q4 + 3]}, inv);
+    if (a.lse && h == 0) a.lse[(size_t(b) * a.Hq + hq) * a.S + i] = (mm + __log2f(ll)) * kLn2;
   };
 
-  // tile t lives in register stage t & 1 until it is stored to LDS buffer
-  // t & 1; its load is issued two tiles ahead of its use, so two tiles of
-  // MFMA work cover its latency
-  const int ntiles = (k_end - k_begin + TK - 1) / TK;
-  // A wave whose row blocks are all padding (G*S rows short of the NW*32 the
-  // workgroup covers) only helps stage the tiles: its scores would never be
-  // stored (2-3% off the attention at 56 and 32 rows per KV head).
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: a scalar branch
-  bool wave_live = false;
-#pragma unroll
-  for (int j = 0; j < RB; ++j) wave_live |= row0 + (wave_s + NW * j) * 32 < rows;
-  load_tile(0, k_begin);
-  if (ntiles > 1) load_tile(1, k_begin + TK);
-  store_tile(0, 0);
-  __syncthreads();
-  // the stage index is a literal at each call (register arrays cannot be
-  // indexed at run time without going to scratch), hence the loop by two
-  auto step = [&](int t, int buf) {
-    if (t + 2 < ntiles) load_tile(buf, k_begin + (t + 2) * TK);  // stage buf held tile t, already in LDS
-    if (wave_live) compute_tile(buf, k_begin + t * TK);
-    if (t + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
-    __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, 0);
-    if (t + 1 < ntiles) step(t + 1, 1);
+  if (a.nsplit == 1) {
+    if (wave_live) store_out(o, m, l);
+    return;
   }
-  // epilogue: o[j][dt][v] = O^T[d = 32dt + 8(v/4) + 4h + v%4][query l32]
+  // split partial: this wave's O^T registers, m and l, in the lanes' own
+  // layout (value e of every lane in one 256-byte run); merged by
+  // block_attn_bf16_merge_kernel
+  if (!wave_live) return;
+  constexpr int PS = attn_pslot(DH);
+  const int npairs = a.B * a.Hkv;
+  float* pp = a.part_o + ((size_t(split) * npairs + pid) * NW + wave) * PS * 64 + lane;
+  if (k_begin < lk) {
 #pragma unroll
-  for (int j = 0; j < RB; ++j) {
-    const int r = row0 + (wave + NW * j) * 32 + l32;
-    if (r >= rows) continue;
-    const int hq = g * a.G + r / a.S, i = r % a.S;
-    const size_t row = (size_t(b) * a.Hq + hq) * a.S + i;
-    if (a.nsplit == 1) {
-      const float inv = 1.f / l[j];
-      T* op = reinterpret_cast<T*>(a.out) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int e = 0; e < 16; ++e) pp[(dt * 16 + e) * 64] = o[dt][e];
+  }
+  pp[(PS - 2) * 64] = m;
+  pp[(PS - 1) * 64] = l;
+}
+
+// Merge of the bf16 kernel's split partials: one wave per (KV head, 32-row
+// block, four O^T registers), lane = (query column, half) exactly as in the
+// attention kernel, so every load is a 256-byte run.  The (m, l) and four
+// values of up to 16 splits are fetched in one round of loads; splits are
+// combined in split order.
+template <int DH, int NW>
+__global__ __launch_bounds__(64) void block_attn_bf16_merge_kernel(AttnArgs a) {
+  if (gate_closed(a.gate)) return;
+  typedef bf16_t T;
+  constexpr int PS = attn_pslot(DH), NQ = DH / 8;  // NQ groups of four values per lane
+  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
+  const int qg = blockIdx.x % NQ, wave = (blockIdx.x / NQ) % NW, pid = blockIdx.x / (NQ * NW);
+  const int rows = a.G * a.S;
+  if (wave * 32 >= rows) return;
+  const int g = pid % a.Hkv, b = pid / a.Hkv;
+  const int npairs = a.B * a.Hkv;
+  constexpr int U = 16;
+  float mmax = -INFINITY, lsum = 0.f;
+  f32x4 acc{0, 0, 0, 0};
+  for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+    float mv[U], lv[U];
+    f32x4 ov[U];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          store4(op + dt * 32 + q4 * 8 + h * 4,
-                 f32x4{o[j][dt][4 * q4], o[j][dt][4 * q4 + 1], o[j][dt][4 * q4 + 2], o[j][dt][4 * q4 + 3]}, inv);
-      if (a.lse && h == 0) a.lse[row] = (m[j] + __log2f(l[j])) * kLn2;
-    } else {
-      float* po = a.part_o + (size_t(split) * a.B * a.Hq * a.S + row) * DH;
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < a.nsplit;
+      const float* pp = a.part_o + ((size_t(s0 + u) * npairs + pid) * NW + wave) * PS * 64 + lane;
+      mv[u] = ok ? pp[(PS - 2) * 64] : -INFINITY;
+      lv[u] = ok ? pp[(PS - 1) * 64] : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int e = 0; e < 4; ++e) ov[u][e] = ok ? pp[(4 * qg + e) * 64] : 0.f;
+    }
+    float rmax = mmax;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          store4(po + dt * 32 + q4 * 8 + h * 4,
-                 f32x4{o[j][dt][4 * q4], o[j][dt][4 * q4 + 1], o[j][dt][4 * q4 + 2], o[j][dt][4 * q4 + 3]}, 1.f);
-      if (h == 0) {
-        float* ml = a.part_ml + (size_t(split) * a.B * a.Hq * a.S + row) * 2;
-        ml[0] = m[j];
-        ml[1] = l[j];
-      }
+    for (int u = 0; u < U; ++u)
+      if (lv[u] > 0.f) rmax = fmaxf(rmax, mv[u]);
+    if (rmax > mmax) {  // carry the reference maximum across rounds
+      const float alpha = mmax == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mmax - rmax);
+      lsum *= alpha;
+      acc *= alpha;
+      mmax = rmax;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!(lv[u] > 0.f)) continue;  // an empty split wrote no O
+      const float w = __builtin_amdgcn_exp2f(mv[u] - mmax);
+      lsum += w * lv[u];
+      acc += w * ov[u];
     }
   }
+  const int r = wave * 32 + l32;
+  if (r >= rows) return;
+  const int hq = g * a.G + r / a.S, i = r % a.S;
+  // values 4qg .. 4qg + 3 of the lane = O^T[d = 32(qg/4) + 8(qg%4) + 4h + 0..3][row r]
+  T* op = reinterpret_cast<T*>(a.out) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
+  store4(op + (qg / 4) * 32 + (qg % 4) * 8 + h * 4, acc, 1.f / lsum);
+  if (a.lse && h == 0 && qg == 0) a.lse[(size_t(b) * a.Hq + hq) * a.S + i] = (mmax + __log2f(lsum)) * kLn2;
 }
 
 
-// Merge the split partials of every query row in split order.  The loads of
-// up to sixteen splits are issued together so that their latencies overlap
-// (the partials were written by workgroups on other XCDs and come back from
-// beyond L2): one round of memory latency for the usual split counts.
+// f32 data: merge the split partials of every query row in split order.  The
+// loads of up to sixteen splits are issued together so that their latencies
+// overlap: one round of memory latency for the usual split counts.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void block_attn_merge_kernel(AttnArgs a) {
   if (gate_closed(a.gate)) return;
@@ -746,10 +827,17 @@ struct AttnPlan {
 
 static int n_row_blocks(const fdl_dims& d) { return (d.n_q_heads / d.n_kv_heads * d.sub_block + 15) / 16; }
 
+// bf16: waves of 32 query rows, at least two (the second only loads when the
+// KV head has at most 32 rows), a power of two
+static int bf16_waves(const fdl_dims& d) {
+  const int rows = d.n_q_heads / d.n_kv_heads * d.sub_block;
+  return rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
+}
+
 static AttnPlan plan_for(const fdl_dims& d, int lk) {
   AttnPlan p;
   const int nrb = n_row_blocks(d);
-  if (d.dtype == FDL_BF16) p.nw = nrb <= 8 ? 4 : 8, p.rb = 1;   // 32-row blocks, <= 128 / 256 rows
+  if (d.dtype == FDL_BF16) p.nw = bf16_waves(d), p.rb = 1;
   else if (nrb <= 1) p.nw = 1, p.rb = 1;
   else if (nrb <= 2) p.nw = 2, p.rb = 1;
   else if (nrb <= 4) p.nw = 4, p.rb = 1;
@@ -778,9 +866,15 @@ static int max_splits(const fdl_dims& d) {
   return tiles < want ? tiles : want;
 }
 
+static size_t bf16_split_bytes(const fdl_dims& d, int nsplit) {
+  const int pairs = d.batch * d.n_kv_heads, nw = bf16_waves(d);
+  return size_t(nsplit) * pairs * nw * attn_pslot(d.head_dim) * 64 * sizeof(float);
+}
+
 size_t attn_workspace_bytes(const fdl_dims& d) {
   const int ns = max_splits(d);
   if (ns <= 1) return 0;
+  if (d.dtype == FDL_BF16) return bf16_split_bytes(d, ns);
   const size_t rows = size_t(d.batch) * d.n_q_heads * d.sub_block;
   return size_t(ns) * rows * (d.head_dim + 2) * sizeof(float);
 }
@@ -800,10 +894,18 @@ static void launch_merge(const AttnArgs& a, hipStream_t st) {
 
 template <int DH>
 static void launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
-  dim3 grid(p.nsplit, a.Hkv, a.B);
-  if (p.nw == 8) hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 8>), grid, dim3(512), 0, st, a);
-  else hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 4>), grid, dim3(256), 0, st, a);
-  if (p.nsplit > 1) launch_merge<bf16_t, DH>(a, st);
+  const dim3 grid(p.nsplit * a.Hkv * a.B);  // one workgroup per (KV head, split); see the logical id
+  const dim3 mgrid(DH / 8 * p.nw * a.Hkv * a.B);  // merge: one wave per (KV head, 32-row block, 4 values)
+  if (p.nw == 8) {
+    hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 8>), grid, dim3(512), 0, st, a);
+    if (p.nsplit > 1) hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, 8>), mgrid, dim3(64), 0, st, a);
+  } else if (p.nw == 4) {
+    hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 4>), grid, dim3(256), 0, st, a);
+    if (p.nsplit > 1) hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, 4>), mgrid, dim3(64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 2>), grid, dim3(128), 0, st, a);
+    if (p.nsplit > 1) hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, 2>), mgrid, dim3(64), 0, st, a);
+  }
 }
 
 template <int DH>
@@ -840,7 +942,10 @@ int attn_launch(const fdl_dims& d, int block_idx, const void* q, const void* kc,
   a.scale_log2 = kLog2e / sqrtf(float(d.head_dim));
   a.part_o = nullptr; a.part_ml = nullptr;
   a.gate = gate;
-  if (p.nsplit > 1) {
+  if (p.nsplit > 1 && d.dtype == FDL_BF16) {
+    if (!ws || ws_bytes < bf16_split_bytes(d, p.nsplit)) return FDL_E_WORKSPACE;
+    a.part_o = reinterpret_cast<float*>(ws);  // the split partials (O, m, l per lane)
+  } else if (p.nsplit > 1) {
     const size_t rows = size_t(d.batch) * d.n_q_heads * d.sub_block;
     const size_t need = size_t(p.nsplit) * rows * (d.head_dim + 2) * sizeof(float);
     if (!ws || ws_bytes < need) return FDL_E_WORKSPACE;

@@ -1,9 +1,12 @@
 """Device buffers and call sequence of a workload's denoising steps.
 
-A step is the whole hot path over one batch: fdl_block_attn, fdl_lm_head,
-fdl_conf_select and, after the last step of a block, fdl_kv_append.  For the
-v1 DualCache workload every block starts with the refresh, which rewrites the
-whole cache through fdl_kv_append (len = 0, then P + L positions).
+A step is the whole hot path over one batch: fdl_block_attn, the LM head and
+the select (fdl_lm_head_select, or fdl_lm_head then fdl_conf_select) and,
+after the last step of a block, fdl_kv_append, which writes the block's K/V at
+each sequence's device-side length and advances it.  For the v1 DualCache
+workload every block starts instead with the refresh, which rewrites all
+P + L cached positions through fdl_kv_write (position 0, len set to P + L in
+the same launch); nothing is appended there.
 
 The hidden rows fed to the LM head are synthetic (the transformer layers
 between attention and the LM head are not part of the step), so the attention
@@ -113,7 +116,8 @@ class StepRunner:
         ws_a = fdl.fdl_block_attn_workspace_size(self.dims)
         ws_s = max(fdl.fdl_conf_select_workspace_size(self.dims, S),
                    fdl.fdl_lm_head_select_workspace_size(self.dims, S))
-        self.ws_attn = torch.empty((max(ws_a, 16),), dtype=torch.uint8, device=self.dev)
+        # the attention workspace starts zeroed: it holds the split counters
+        self.ws_attn = torch.zeros((max(ws_a, 16),), dtype=torch.uint8, device=self.dev)
         self.ws_sel = torch.empty((max(ws_s, 16),), dtype=torch.uint8, device=self.dev)
 
     # -- the step ------------------------------------------------------------
@@ -149,12 +153,10 @@ class StepRunner:
                                inp.masked, self.ws_sel)
 
     def append(self, i: int):
-        """Store the finished block b.  The batch moves in lock-step (every
-        sequence's block b starts at P + b*D), so the position is known here
-        and the write needs no device-side length: one launch."""
+        """Store the finished block b at every sequence's length and advance
+        it (fdl_kv_append: one launch for a block's worth of K/V)."""
         b = self.inputs[i].block_idx
-        fdl.fdl_kv_write(self.dims, self.k_cache, self.v_cache, self.k_blk[b], self.v_blk[b],
-                         self.cfg.prompt_len + b * self.cfg.block, self.len)
+        fdl.fdl_kv_append(self.dims, self.k_cache, self.v_cache, self.k_blk[b], self.v_blk[b], self.len)
 
     def step(self, i: int):
         inp = self.inputs[i]

@@ -123,7 +123,9 @@ const char* fdl_strerror(int status);
 int fdl_dims_check(const fdl_dims* dims);
 
 /* Bytes of device workspace fdl_block_attn needs for any block_idx/sub_idx
- * of `dims` (0 if none).  Returns 0 for invalid dims. */
+ * of `dims` (0 if none).  Returns 0 for invalid dims.  The workspace holds
+ * the key splits' partial results (scratch of one call: calls that overlap
+ * on one workspace race). */
 size_t fdl_block_attn_workspace_size(const fdl_dims* dims);
 
 /* Block attention: eq 3 (softmax(Q K^T / sqrt(d)) V) over the visible keys of

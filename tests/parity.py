@@ -1,6 +1,9 @@
 """Comparison rules between the HIP path and the oracle (test-only helpers).
 
-Floating point: normwise max error, max|g - o| / max|o| per output tensor.
+Floating point: normwise max error, max|g - o| / max|o| per output tensor,
+and for attention outputs per query row (the scale is that row's own max|o|
+over its d elements, so a row with small outputs is held to the same
+relative bound as the tensor's largest).
 Integers (token ids, commit sets, counts): bit-exact, except positions the
 rules exclude because their decision sits within `eps` of a boundary in the
 oracle's own values:
@@ -25,6 +28,21 @@ def normwise(got, ref) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     scale = np.abs(ref).max()
     return float(np.abs(got - ref).max() / (scale if scale > 0 else 1.0))
+
+
+def rowwise(got, ref) -> dict:
+    """Per-row normwise error over the last axis: for each row,
+    max_d |g - o| / max_d |o|.  Returns the worst row's error ("max") with
+    element-wise diagnostics: the largest absolute error, the median and 99th
+    percentile of the per-row errors, and the row count."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = ref.shape[-1]
+    g2, r2 = got.reshape(-1, d), ref.reshape(-1, d)
+    scale = np.abs(r2).max(axis=1)
+    err = np.abs(g2 - r2).max(axis=1) / np.where(scale > 0, scale, 1.0)
+    return dict(max=float(err.max()), p50=float(np.median(err)), p99=float(np.percentile(err, 99)),
+                abs_max=float(np.abs(g2 - r2).max()), rows=int(err.size))
 
 
 def compare_select(ref: dict, got: dict, masked, tau, mode=O.SELECT_THRESHOLD, k=0, factor=1.0,

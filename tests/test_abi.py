@@ -66,7 +66,17 @@ def test_workspace_sizes(L):
         d = fdl.make_dims(cfg)
         ws = fdl.fdl_block_attn_workspace_size(d)
         rows = cfg.batch * cfg.n_q_heads * cfg.sub_block
-        assert ws == 0 or ws % (rows * (cfg.head_dim + 2) * 4) == 0
+        if cfg.dtype == "f32":
+            # split partials (m, l, O) per query row
+            assert ws == 0 or ws % (rows * (cfg.head_dim + 2) * 4) == 0
+        else:
+            # per split, KV head and 64-lane wave of 32 rows: the wave's O registers,
+            # m and l (d/2 + 2 floats per lane)
+            pairs = cfg.batch * cfg.n_kv_heads
+            g_rows = cfg.n_q_heads // cfg.n_kv_heads * cfg.sub_block
+            nw = 2 if g_rows <= 64 else 4 if g_rows <= 128 else 8
+            per_split = pairs * nw * 64 * (cfg.head_dim // 2 + 2) * 4
+            assert ws == 0 or (ws % per_split == 0 and ws > 0), (name, ws)
         assert fdl.fdl_conf_select_workspace_size(d, cfg.sub_block) >= cfg.batch * cfg.sub_block * 16
     assert fdl.fdl_block_attn_workspace_size(_dims(batch=0)) == 0
     assert fdl.fdl_conf_select_workspace_size(_dims(), 0) == 0

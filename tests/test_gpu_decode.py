@@ -220,6 +220,9 @@ def test_decode_workload_shapes_bf16(name, max_blocks):
     ref = _oracle(run)
     res = _compare(run, got, ref)
     print(f"steps {got['steps']} excluded {res['excluded']} forked {res['forked']}", flush=True)
+    # a fork is only allowed at an excluded decision, and not before ten steps
+    # have been compared
+    assert res["forked"] is None or res["forked"] >= 10, res
 
 
 def test_decode_graph_replay():

@@ -9,7 +9,7 @@ import torch
 
 from block_diffusion_decoding_attn_amd import fdl, synth
 from oracle import fdl_oracle as O
-from parity import compare_select, normwise
+from parity import compare_select, normwise, rowwise
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
     kb, vb = synth.block_kv(cfg, block_idx, seed)
     out = torch.empty_like(q, device=dev)
     lse = torch.empty((cfg.batch, cfg.n_q_heads, cfg.sub_block), dtype=torch.float32, device=dev)
-    ws = torch.empty((max(fdl.fdl_block_attn_workspace_size(d), 16),), dtype=torch.uint8, device=dev)
+    ws = torch.zeros((max(fdl.fdl_block_attn_workspace_size(d), 16),), dtype=torch.uint8, device=dev)
     pl = None if prefix is None else torch.tensor(prefix, dtype=torch.int32, device=dev)
     fdl.fdl_block_attn(d, block_idx, sub_idx, q.to(dev), kc.to(dev), vc.to(dev), pl, kb.to(dev), vb.to(dev),
                        out, lse, ws)
@@ -79,8 +79,11 @@ def test_block_attn_parity(kw, block_idx, prefix):
     got_o, got_l, ref_o, ref_l = _attn_case(cfg, block_idx, prefix=prefix)
     tol = TOL[cfg.dtype]
     e_o = normwise(got_o, ref_o)
+    rw = rowwise(got_o, ref_o)
     e_l = np.abs(got_l - ref_l).max() / np.abs(ref_l).max()
+    print(f"attn {kw} block {block_idx}: tensor {e_o:.2e} per-row {rw}", flush=True)
     assert e_o <= tol, e_o
+    assert rw["max"] <= tol, rw
     assert e_l <= (1e-5 if cfg.dtype == "f32" else 1e-3), e_l
 
 
