@@ -4,8 +4,35 @@
 #include "launch.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace fdl {
+
+// Scratch of fdl_lm_head_select_noalloc: a file-scope device array (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// must not pass `scratch` itself to a kernel (that is a host-side stand-in):
+// its device address is looked up once per device with hipGetSymbolAddress
+// and kept per device.
+static __device__ __align__(256) char scratch[FDL_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with it current).
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FDL_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FDL_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FDL_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FDL_OK;
+}
 
 int dtype_size(int dtype) { return dtype == FDL_F32 ? 4 : 2; }
 
@@ -111,6 +138,7 @@ const char* fdl_strerror(int status) {
     case FDL_E_UNSUPPORTED: return "unsupported argument combination";
     case FDL_E_HIP: return "HIP launch error";
     case FDL_E_WORKSPACE: return "workspace missing or too small";
+    case FDL_E_SCRATCH: return "problem needs more than the allocation-free entry point's static scratch";
     default: return "unknown status";
   }
 }
@@ -203,6 +231,33 @@ int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x
   rc = lm_head_launch(d, rows, x, w, logits, workspace, st);
   if (rc != FDL_OK) return rc;
   return select_finalize_launch(d, rows_per_seq, workspace, nc, masked, tau, mode, k, factor, token_out, conf_out,
+                                commit_out, n_commit, tokens_inout, masked_inout, st);
+}
+
+int fdl_lm_head_select_noalloc(const fdl_dims* dims, int32_t rows_per_seq, const void* x, const void* w,
+                               float* logits, const uint8_t* masked, const float* tau, int32_t mode, int32_t k,
+                               float factor, int32_t* token_out, float* conf_out, uint8_t* commit_out,
+                               int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != FDL_OK) return rc;
+  const fdl_dims& d = *dims;
+  rc = check_select_args(d, rows_per_seq, masked, tau, mode, k, factor, token_out, conf_out, commit_out, n_commit);
+  if (rc != FDL_OK) return rc;
+  const int rows = d.batch * rows_per_seq;
+  rc = check_lm_head_args(d, rows, x, w);
+  if (rc != FDL_OK) return rc;
+  const int nc = lm_head_tiles(d, rows);
+  const size_t need = partials_workspace_bytes(d, rows_per_seq, nc);
+  if (need > FDL_NOALLOC_SCRATCH_BYTES) return FDL_E_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FDL_OK) return rc;
+  // the partials' row counters are zeroed by the LM-head kernel itself, so
+  // nothing of the scratch has to be cleared here
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = lm_head_launch(d, rows, x, w, logits, ws, st);
+  if (rc != FDL_OK) return rc;
+  return select_finalize_launch(d, rows_per_seq, ws, nc, masked, tau, mode, k, factor, token_out, conf_out,
                                 commit_out, n_commit, tokens_inout, masked_inout, st);
 }
 

@@ -17,7 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfdl.so")
 
-FDL_OK, FDL_E_INVAL, FDL_E_UNSUPPORTED, FDL_E_HIP, FDL_E_WORKSPACE = 0, -1, -2, -3, -4
+FDL_OK, FDL_E_INVAL, FDL_E_UNSUPPORTED, FDL_E_HIP, FDL_E_WORKSPACE, FDL_E_SCRATCH = 0, -1, -2, -3, -4, -5
+FDL_NOALLOC_SCRATCH_BYTES = 8 << 20
 FDL_F32, FDL_BF16 = 0, 1
 FDL_ATTN_BLOCK_CAUSAL, FDL_ATTN_DUAL_CACHE = 0, 1
 FDL_SELECT_THRESHOLD, FDL_SELECT_TOPK, FDL_SELECT_FACTOR = 0, 1, 2
@@ -26,7 +27,7 @@ EXPORTS = (
     "fdl_version", "fdl_strerror", "fdl_dims_check", "fdl_block_attn_workspace_size", "fdl_block_attn",
     "fdl_prefill_attn",
     "fdl_lm_head", "fdl_conf_select_workspace_size", "fdl_conf_select", "fdl_lm_head_select_workspace_size",
-    "fdl_lm_head_select", "fdl_kv_append", "fdl_kv_write", "fdl_decode_workspace_size", "fdl_decode_step_slots",
+    "fdl_lm_head_select", "fdl_lm_head_select_noalloc", "fdl_kv_append", "fdl_kv_write", "fdl_decode_workspace_size", "fdl_decode_step_slots",
     "fdl_decode",
 )
 
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
             L.fdl_lm_head_select_workspace_size.argtypes = [_D, _I]
             L.fdl_lm_head_select.argtypes = [_D, _I, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_size_t, _P]
+            L.fdl_lm_head_select_noalloc.argtypes = [_D, _I, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P,
+                                                     _P, _P, _P, _P]
             L.fdl_kv_append.argtypes = [_D, _P, _P, _P, _P, _I, _P, _P]
             L.fdl_kv_write.argtypes = [_D, _P, _P, _P, _P, _I, _I, _P, _P]
             L.fdl_decode_workspace_size.restype = ctypes.c_size_t
@@ -274,6 +277,35 @@ def fdl_lm_head_select(dims: fdl_dims, rows_per_seq: int, x, w, logits, masked, 
                                   _ptr(n_commit), _ptr(tokens_inout), _ptr(masked_inout), _ptr(workspace), ws_bytes,
                                   _stream(stream))
     _check("fdl_lm_head_select", rc)
+
+
+def fdl_lm_head_select_noalloc(dims: fdl_dims, rows_per_seq: int, x, w, logits, masked, tau, mode: int, k: int,
+                               factor: float, token_out, conf_out, commit_out, n_commit, tokens_inout=None,
+                               masked_inout=None, stream=None):
+    """fdl_lm_head_select with the library's static scratch instead of a workspace."""
+    d = dims
+    dt = _dtype(d)
+    B, R = d.batch, rows_per_seq
+    _expect("x", x, (B * R, d.hidden), dt)
+    _expect("w", w, (d.vocab, d.hidden), dt)
+    if logits is not None:
+        _expect("logits", logits, (B * R, d.vocab), torch.float32)
+    _expect("masked", masked, (B, R), torch.uint8)
+    if tau is not None:
+        _expect("tau", tau, (B,), torch.float32)
+    _expect("token_out", token_out, (B, R), torch.int32)
+    _expect("conf_out", conf_out, (B, R), torch.float32)
+    _expect("commit_out", commit_out, (B, R), torch.uint8)
+    _expect("n_commit", n_commit, (B,), torch.int32)
+    if tokens_inout is not None:
+        _expect("tokens_inout", tokens_inout, (B, R), torch.int32)
+    if masked_inout is not None:
+        _expect("masked_inout", masked_inout, (B, R), torch.uint8)
+    rc = lib().fdl_lm_head_select_noalloc(ctypes.byref(d), R, _ptr(x), _ptr(w), _ptr(logits), _ptr(masked),
+                                          _ptr(tau), mode, k, factor, _ptr(token_out), _ptr(conf_out),
+                                          _ptr(commit_out), _ptr(n_commit), _ptr(tokens_inout), _ptr(masked_inout),
+                                          _stream(stream))
+    _check("fdl_lm_head_select_noalloc", rc)
 
 
 def fdl_kv_append(dims: fdl_dims, k_cache, v_cache, k_new, v_new, length, stream=None):

@@ -56,7 +56,8 @@ typedef enum {
   FDL_E_INVAL = -1,        /* a scalar or pointer argument is invalid           */
   FDL_E_UNSUPPORTED = -2,  /* valid but not supported (e.g. head_dim 96)        */
   FDL_E_HIP = -3,          /* a HIP launch reported an error                    */
-  FDL_E_WORKSPACE = -4     /* workspace missing or smaller than required        */
+  FDL_E_WORKSPACE = -4,    /* workspace missing or smaller than required        */
+  FDL_E_SCRATCH = -5       /* more than FDL_NOALLOC_SCRATCH_BYTES of scratch    */
 } fdl_status;
 
 typedef enum { FDL_F32 = 0, FDL_BF16 = 1 } fdl_dtype;
@@ -230,6 +231,25 @@ int fdl_lm_head_select(const fdl_dims* dims, int32_t rows_per_seq, const void* x
                        uint8_t* commit_out, int32_t* n_commit, int32_t* tokens_inout,
                        uint8_t* masked_inout, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Allocation-free variant of fdl_lm_head_select, for callers that cannot
+ * allocate or pass device memory for a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments and results as fdl_lm_head_select without the workspace; the
+ * select partials and row counters live in a static device array of the
+ * library (FDL_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends),
+ * so the call allocates nothing.  Returns FDL_E_SCRATCH, launching nothing,
+ * when fdl_lm_head_select_workspace_size(dims, rows_per_seq) exceeds that
+ * size.  Every call on a GPU shares that GPU's array: calls that overlap on
+ * one GPU (concurrent streams or host threads) race.  The array's address is
+ * looked up on the first call on each device (with that device current). */
+#define FDL_NOALLOC_SCRATCH_BYTES (8u << 20)
+int fdl_lm_head_select_noalloc(const fdl_dims* dims, int32_t rows_per_seq, const void* x,
+                               const void* w, float* logits, const uint8_t* masked,
+                               const float* tau, int32_t mode, int32_t k, float factor,
+                               int32_t* token_out, float* conf_out, uint8_t* commit_out,
+                               int32_t* n_commit, int32_t* tokens_inout, uint8_t* masked_inout,
+                               void* stream);
 
 /* KV append ("Fast-dLLM v2", Level 3 block-level cache: a finished block's
  * K/V are stored for all later steps; Fast-dLLM Algorithm 1: the refresh

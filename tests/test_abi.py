@@ -206,3 +206,16 @@ def test_decode_rejects_before_launch(L):
     assert call(dims=_dims(hidden=3520)) == -2                    # stand-in model needs H = Hq * d
     assert call(wsz=ws - 1) == -4
     assert call(w=None) == -4
+
+
+def test_noalloc_rejects_oversized_problem(L):
+    """The allocation-free LM head + select refuses, before any launch, a
+    problem whose select partials exceed the library's static scratch."""
+    cfg = synth.small_variant(synth.get_config("qwen2.5-7b_long_bs16"), vocab=1 << 24, hidden=64)
+    d = fdl.make_dims(cfg)
+    assert fdl.fdl_lm_head_select_workspace_size(d, 32) > fdl.FDL_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    rc = L.fdl_lm_head_select_noalloc(ctypes.byref(d), 32, fake, fake, None, fake, fake, fdl.FDL_SELECT_THRESHOLD,
+                                      0, ctypes.c_float(1.0), fake, fake, fake, fake, None, None, None)
+    assert rc == fdl.FDL_E_SCRATCH
+    assert "scratch" in fdl.fdl_strerror(rc)
