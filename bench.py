@@ -363,6 +363,60 @@ def exceed_tau(run, cfg, other_boost: str, n_steps: int = 8):
     return above / max(cands, 1), n_steps
 
 
+def _pmc_per_kernel(db, counter):
+    """{kernel name: (dispatches, mean per-dispatch value)} of one rocprofv3
+    --pmc results database (values summed over a dispatch's records)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, dispatch_id, sum(value) from counters_collection "
+                       "where counter_name = ? group by dispatch_id", (counter,)).fetchall()
+    out = {}
+    for name, _, v in rows:
+        n, tot = out.get(name, (0, 0.0))
+        out[name] = (n + 1, tot + v)
+    return {k: (n, tot / n) for k, (n, tot) in out.items()}
+
+
+def summarize_pmc(args):
+    """Write the FETCH_SIZE / WRITE_SIZE summary that pmc_traffic() reads, from
+    four rocprofv3 --pmc databases: the workload's FETCH_SIZE and WRITE_SIZE
+    runs and the same two counters over the calibration copy."""
+    fetch_db, write_db, cal_fetch_db, cal_write_db = args.summarize_pmc
+    kernel = args.pmc_kernel
+    names = ["block_attn_bf16_kernel", "block_attn_bf16_merge_kernel"] if kernel == "attn" else [
+        lm_head_kernel_name(__import__("block_diffusion_decoding_attn_amd.synth", fromlist=["x"]).get_config(
+            args.workload))]
+    src = ATTN_SRC if kernel == "attn" else LM_HEAD_SRC
+
+    def pick(db, counter):
+        got = _pmc_per_kernel(db, counter)
+        n, tot = 0, 0.0
+        for nm in names:
+            hits = [(k, v) for k, v in got.items() if nm + "<" in k or nm + "(" in k]
+            if hits:
+                k, (cnt, val) = max(hits, key=lambda kv: kv[1][0])
+                n = max(n, cnt)
+                tot += val
+        return n, tot
+
+    nf, fetch = pick(fetch_db, "FETCH_SIZE")
+    nw, write = pick(write_db, "WRITE_SIZE")
+    cal_f = max(_pmc_per_kernel(cal_fetch_db, "FETCH_SIZE").items(), key=lambda kv: kv[1][1])[1][1]
+    cal_w = max(_pmc_per_kernel(cal_write_db, "WRITE_SIZE").items(), key=lambda kv: kv[1][1])[1][1]
+    mib = args.pmc_copy_mib
+    sf, sw = mib * 1024 / cal_f, mib * 1024 / cal_w
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    lines = [f"kernel: {' + '.join(names)}", f"workload: {args.workload}",
+             f"source: {os.path.relpath(src, ROOT)}", f"source_sha256: {sha}",
+             f"dispatches_fetch: {nf}", f"dispatches_write: {nw}",
+             f"fetch_kib_per_dispatch: {fetch:.1f}", f"write_kib_per_dispatch: {write:.1f}",
+             f"copy_fetch_kib_per_dispatch: {cal_f:.1f}", f"copy_write_kib_per_dispatch: {cal_w:.1f}",
+             f"copy_fetch_scale: {sf:.4f}", f"copy_write_scale: {sw:.4f}",
+             f"fetch_bytes_per_dispatch: {fetch * 1024 * sf:.0f}",
+             f"write_bytes_per_dispatch: {write * 1024 * sw:.0f}"]
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,7 +436,15 @@ def main():
                     help="with --decode-loop: capture the generation in a HIP graph and time its replays")
     ap.add_argument("--calibrate-counters", type=int, nargs="?", const=1024, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 4 times (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="print the counter-traffic summary of --pmc-kernel on --workload from four rocprofv3 "
+                         "--pmc databases (no GPU needed)")
+    ap.add_argument("--pmc-kernel", default="attn", choices=["attn", "lm_head"])
+    ap.add_argument("--pmc-copy-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.calibrate_counters is not None:
         calibrate_counters(args.calibrate_counters)
         return

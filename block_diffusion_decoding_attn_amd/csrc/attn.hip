@@ -704,28 +704,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   pp[(PS - 1) * 64] = l;
 }
 
-// Merge of the bf16 kernel's split partials: one wave per (KV head, 32-row
-// block, four O^T registers), lane = (query column, half) exactly as in the
-// attention kernel, so every load is a 256-byte run.  The (m, l) and four
-// values of up to 16 splits are fetched in one round of loads; splits are
-// combined in split order.
-template <int DH, int NW>
-__global__ __launch_bounds__(64) void block_attn_bf16_merge_kernel(AttnArgs a) {
+// Merge of the bf16 kernel's split partials: one workgroup per (KV head,
+// 32-row block) of d / (2 NE) waves; wave j of it merges the lanes' values
+// NE j .. NE j + NE - 1 of the attention wave's O^T registers.  Lane = (query
+// column, half) exactly as in the attention kernel, so every load is a
+// 256-byte run.  The (m, l) and values of up to U splits are fetched in one
+// round of loads; splits are combined in split order.  Few splits: NE = 16,
+// U = 4, the d / 32 waves of a row block in one workgroup (they share its
+// (m, l) loads); many splits: NE = 4, U = 16 (one round), one wave per
+// workgroup, so that the loads of few row blocks spread over many CUs.
+template <int DH, int NW, int NE, int U, int NWG>
+__global__ __launch_bounds__(NWG * 64) void block_attn_bf16_merge_kernel(AttnArgs a) {
   if (gate_closed(a.gate)) return;
   typedef bf16_t T;
-  constexpr int PS = attn_pslot(DH), NQ = DH / 8;  // NQ groups of four values per lane
-  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
-  const int qg = blockIdx.x % NQ, wave = (blockIdx.x / NQ) % NW, pid = blockIdx.x / (NQ * NW);
+  constexpr int PS = attn_pslot(DH), NJ = DH / 2 / NE;  // waves per row block
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  const int blk = blockIdx.x / (NJ / NWG);
+  const int j = (threadIdx.x >> 6) + NWG * (blockIdx.x % (NJ / NWG));
+  const int wave = blk % NW, pid = blk / NW;
   const int rows = a.G * a.S;
   if (wave * 32 >= rows) return;
   const int g = pid % a.Hkv, b = pid / a.Hkv;
   const int npairs = a.B * a.Hkv;
-  constexpr int U = 16;
   float mmax = -INFINITY, lsum = 0.f;
-  f32x4 acc{0, 0, 0, 0};
+  float acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < a.nsplit; s0 += U) {
-    float mv[U], lv[U];
-    f32x4 ov[U];
+    float mv[U], lv[U], ov[U][NE];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = s0 + u < a.nsplit;
@@ -733,7 +739,7 @@ __global__ __launch_bounds__(64) void block_attn_bf16_merge_kernel(AttnArgs a) {
       mv[u] = ok ? pp[(PS - 2) * 64] : -INFINITY;
       lv[u] = ok ? pp[(PS - 1) * 64] : 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ov[u][e] = ok ? pp[(4 * qg + e) * 64] : 0.f;
+      for (int e = 0; e < NE; ++e) ov[u][e] = ok ? pp[(NE * j + e) * 64] : 0.f;
     }
     float rmax = mmax;
 #pragma unroll
@@ -742,7 +748,8 @@ __global__ __launch_bounds__(64) void block_attn_bf16_merge_kernel(AttnArgs a) {
     if (rmax > mmax) {  // carry the reference maximum across rounds
       const float alpha = mmax == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mmax - rmax);
       lsum *= alpha;
-      acc *= alpha;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       mmax = rmax;
     }
 #pragma unroll
@@ -750,16 +757,22 @@ __global__ __launch_bounds__(64) void block_attn_bf16_merge_kernel(AttnArgs a) {
       if (!(lv[u] > 0.f)) continue;  // an empty split wrote no O
       const float w = __builtin_amdgcn_exp2f(mv[u] - mmax);
       lsum += w * lv[u];
-      acc += w * ov[u];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[e] += w * ov[u][e];
     }
   }
   const int r = wave * 32 + l32;
   if (r >= rows) return;
   const int hq = g * a.G + r / a.S, i = r % a.S;
-  // values 4qg .. 4qg + 3 of the lane = O^T[d = 32(qg/4) + 8(qg%4) + 4h + 0..3][row r]
+  // value NE*j + e of the lane = O^T[d = 32 dt + 8 (v/4) + 4h + v%4][row r], dt = (NE*j + e) / 16, v = (..) % 16
   T* op = reinterpret_cast<T*>(a.out) + ((size_t(b) * a.S + i) * a.Hq + hq) * DH;
-  store4(op + (qg / 4) * 32 + (qg % 4) * 8 + h * 4, acc, 1.f / lsum);
-  if (a.lse && h == 0 && qg == 0) a.lse[(size_t(b) * a.Hq + hq) * a.S + i] = (mmax + __log2f(lsum)) * kLn2;
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int e4 = 0; e4 < NE; e4 += 4) {
+    const int e = NE * j + e4, dt = e / 16, v = e % 16;
+    store4(op + dt * 32 + (v / 4) * 8 + h * 4, f32x4{acc[e4], acc[e4 + 1], acc[e4 + 2], acc[e4 + 3]}, inv);
+  }
+  if (a.lse && h == 0 && j == 0) a.lse[(size_t(b) * a.Hq + hq) * a.S + i] = (mmax + __log2f(lsum)) * kLn2;
 }
 
 
@@ -892,19 +905,29 @@ static void launch_merge(const AttnArgs& a, hipStream_t st) {
                      dim3(256), 0, st, a);
 }
 
+template <int DH, int NW>
+static void launch_merge_bf16(const AttnArgs& a, hipStream_t st) {
+  const int blocks = NW * a.Hkv * a.B;  // (KV head, 32-row block) pairs
+  if (a.nsplit <= 4)
+    hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, NW, 16, 4, DH / 32>), dim3(blocks), dim3(DH / 32 * 64), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, NW, 4, 16, 1>), dim3(blocks * (DH / 8)), dim3(64), 0, st,
+                       a);
+}
+
 template <int DH>
 static void launch_attn_bf16(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const dim3 grid(p.nsplit * a.Hkv * a.B);  // one workgroup per (KV head, split); see the logical id
-  const dim3 mgrid(DH / 8 * p.nw * a.Hkv * a.B);  // merge: one wave per (KV head, 32-row block, 4 values)
   if (p.nw == 8) {
     hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 8>), grid, dim3(512), 0, st, a);
-    if (p.nsplit > 1) hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, 8>), mgrid, dim3(64), 0, st, a);
+    if (p.nsplit > 1) launch_merge_bf16<DH, 8>(a, st);
   } else if (p.nw == 4) {
     hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 4>), grid, dim3(256), 0, st, a);
-    if (p.nsplit > 1) hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, 4>), mgrid, dim3(64), 0, st, a);
+    if (p.nsplit > 1) launch_merge_bf16<DH, 4>(a, st);
   } else {
     hipLaunchKernelGGL((block_attn_bf16_kernel<DH, 2>), grid, dim3(128), 0, st, a);
-    if (p.nsplit > 1) hipLaunchKernelGGL((block_attn_bf16_merge_kernel<DH, 2>), mgrid, dim3(64), 0, st, a);
+    if (p.nsplit > 1) launch_merge_bf16<DH, 2>(a, st);
   }
 }
 
