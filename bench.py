@@ -417,6 +417,48 @@ def summarize_pmc(args):
     print("\n".join(lines))
 
 
+def summarize_trace(db):
+    """Print per-kernel duration statistics (markdown) of a rocprofv3
+    --kernel-trace results database (no GPU needed)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                       "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[5] for r in rows) or 1
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|")
+    for name, n, avg, lo, hi, tot in rows[:12]:
+        print(f"| `{name[:80]}` | {n} | {avg / 1e3:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} | {100.0 * tot / total:.1f}% |")
+
+
+def summarize_counters(db):
+    """Print, per kernel and counter, the mean per-dispatch value (records of a
+    dispatch summed) and the mean duration of a rocprofv3 --pmc database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, counter_name, dispatch_id, sum(value) from counters_collection "
+                       "group by kernel_name, counter_name, dispatch_id").fetchall()
+    acc = {}
+    for name, ctr, _, v in rows:
+        n, tot = acc.get((name, ctr), (0, 0.0))
+        acc[(name, ctr)] = (n + 1, tot + v)
+    kernels = sorted({k for k, _ in acc}, key=lambda k: -max(n for (kk, _), (n, _) in acc.items() if kk == k))
+    ctrs = sorted({c for _, c in acc})
+    dur = {}
+    try:
+        for name, avg in con.execute("select name, avg(duration) from kernels group by name"):
+            dur[name] = avg / 1e3
+    except sqlite3.Error:
+        pass
+    print("| kernel | dispatches | us | " + " | ".join(ctrs) + " |")
+    print("|---|---|---|" + "---|" * len(ctrs))
+    for k in kernels[:12]:
+        n = max(acc[(k, c)][0] for c in ctrs if (k, c) in acc)
+        vals = [f"{acc[(k, c)][1] / acc[(k, c)][0]:.6g}" if (k, c) in acc else "" for c in ctrs]
+        us = f"{dur[k]:.2f}" if k in dur else ""
+        print(f"| `{k[:80]}` | {n} | {us} | " + " | ".join(vals) + " |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,11 +481,21 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="print the counter-traffic summary of --pmc-kernel on --workload from four rocprofv3 "
                          "--pmc databases (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DB",
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace database (no GPU needed)")
+    ap.add_argument("--summarize-counters", metavar="PMC_DB",
+                    help="print per-kernel mean counter values from a rocprofv3 --pmc database (no GPU needed)")
     ap.add_argument("--pmc-kernel", default="attn", choices=["attn", "lm_head"])
     ap.add_argument("--pmc-copy-mib", type=int, default=1024)
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.calibrate_counters is not None:
         calibrate_counters(args.calibrate_counters)

@@ -509,7 +509,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m = -INFINITY, l = 0.f;  // l: this lane's share of the row sum
+  float m = -INFINITY;
+  float lw[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's share of the row sum, in four independent chains
 
   if (k_begin < lk) {
     // this lane's share of the wave's load instructions.  A wave's IPW
@@ -593,16 +594,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           for (int v = 0; v < 16; ++v)
             if (key0 + kt * 32 + (v / 4) * 8 + h * 4 + (v % 4) >= k_end) s[kt][v] = -INFINITY;
       }
-      float mx = fmaxf(s[0][0], s[0][1]);
+      // four independent max chains (a single chain of dependent max3 would
+      // expose the VALU latency at every step)
+      float mq[4];
 #pragma unroll
-      for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[0][v]), s[0][v + 1]);
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[1][v]), s[1][v + 1]);
+      for (int qd = 0; qd < 4; ++qd) {
+        const int kt = qd >> 1, v0 = (qd & 1) * 8;
+        mq[qd] = fmaxf(fmaxf(s[kt][v0], s[kt][v0 + 1]), s[kt][v0 + 2]);
+        mq[qd] = fmaxf(fmaxf(mq[qd], s[kt][v0 + 3]), s[kt][v0 + 4]);
+        mq[qd] = fmaxf(fmaxf(mq[qd], s[kt][v0 + 5]), s[kt][v0 + 6]);
+        mq[qd] = fmaxf(mq[qd], s[kt][v0 + 7]);
+      }
+      float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       mx = xor32_max(mx) * c;
       if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
         const float mn = fmaxf(m, mx);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        l *= alpha;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lw[w] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         m = mn;
@@ -621,7 +630,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             // (a named value: a bit cast of the vector element pf[w] reads element 0)
             const uint32_t pw = pack_bf16x2(p0, p1);
             pf[w] = pw;
-            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, l, false);
+            lw[w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, lw[w], false);
           }
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
@@ -666,7 +675,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       if (wave_live) compute(t);
     }
   }
-  l = xor32_sum(l);  // both half-waves' shares of the row sum
+  float l = xor32_sum((lw[0] + lw[1]) + (lw[2] + lw[3]));  // both half-waves' shares of the row sum
 
   // o[dt][v] = O^T[d = 32dt + 8(v/4) + 4h + v%4][query row r]
   auto store_out = [&](const f32x16* oo, float mm, float ll) __attribute__((always_inline)) {

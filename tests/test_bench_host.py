@@ -95,3 +95,85 @@ def test_counter_traffic_only_for_its_workload_and_source(name):
     else:
         # tiled: at least the algorithmic bytes (row tiles of a weight tile share one XCD's L2)
         assert got >= 0.99 * byts
+
+
+def test_attention_counter_summary_long_context():
+    """The long-context attention summary: K/V leave HBM once; the rest of the
+    counted traffic is the fp32 split partials (written by the attention,
+    read back by the merge) and Q / O."""
+    name = "qwen2.5-7b_long_bs16"
+    path = bench.pmc_profile(name, "attn")
+    assert os.path.exists(path)
+    kv = _pmc_fields(path)
+    assert kv["workload"] == name
+    assert kv["kernel"] == "block_attn_bf16_kernel + block_attn_bf16_merge_kernel"
+    cfg = synth.get_config(name)
+    lk = cfg.prompt_len + cfg.block
+    pairs = cfg.batch * cfg.n_kv_heads
+    rows = cfg.n_q_heads // cfg.n_kv_heads * cfg.sub_block  # query rows per KV head
+    live_waves = (rows + 31) // 32
+    nsplit = 4                                           # 256 workgroups over 64 KV heads
+    partials = nsplit * pairs * live_waves * (cfg.head_dim // 2 + 2) * 64 * 4
+    q = cfg.batch * cfg.sub_block * cfg.n_q_heads * cfg.head_dim * 2
+    kvb = 2 * pairs * lk * cfg.head_dim * 2
+    assert bench.attn_bytes(cfg, lk) == kvb + 2 * q
+    fetch = float(kv["fetch_bytes_per_dispatch"])
+    write = float(kv["write_bytes_per_dispatch"])
+    assert abs(fetch - (kvb + q + partials)) / kvb < 0.02
+    assert abs(write - (partials + q)) / (partials + q) < 0.02
+
+
+def _sqlite(path, tables):
+    import sqlite3
+    con = sqlite3.connect(path)
+    for name, cols, rows in tables:
+        con.execute(f"create table {name}({', '.join(cols)})")
+        con.executemany(f"insert into {name} values ({', '.join('?' * len(cols))})", rows)
+    con.commit()
+    con.close()
+
+
+def test_summarize_trace_and_counters(tmp_path, capsys):
+    tr = str(tmp_path / "t.db")
+    _sqlite(tr, [("kernels", ["name", "duration"], [("k_a", 3000), ("k_a", 5000), ("k_b", 1000)])])
+    bench.summarize_trace(tr)
+    out = capsys.readouterr().out.splitlines()
+    assert out[2] == "| `k_a` | 2 | 4.00 | 3.00 | 5.00 | 88.9% |"
+    assert out[3] == "| `k_b` | 1 | 1.00 | 1.00 | 1.00 | 11.1% |"
+    pc = str(tmp_path / "c.db")
+    _sqlite(pc, [("counters_collection", ["kernel_name", "counter_name", "dispatch_id", "value"],
+                  [("k_a", "X", 1, 2.0), ("k_a", "X", 1, 3.0), ("k_a", "X", 2, 7.0), ("k_a", "Y", 1, 1.0),
+                   ("k_a", "Y", 2, 3.0)]),
+                 ("kernels", ["name", "duration"], [("k_a", 2000), ("k_a", 4000)])])
+    bench.summarize_counters(pc)
+    out = capsys.readouterr().out.splitlines()
+    # dispatch 1: X = 2 + 3 (records summed), dispatch 2: X = 7 -> mean 6; Y mean 2
+    assert out[2] == "| `k_a` | 2 | 3.00 | 6 | 2 |"
+
+
+def test_summarize_pmc_scales_by_the_copy(tmp_path, capsys):
+    rows_f = [("void fdl::block_attn_bf16_kernel<128, 8>(fdl::AttnArgs)", "FETCH_SIZE", d, v)
+              for d, v in [(1, 100.0), (1, 50.0), (2, 150.0)]]
+    rows_f += [("void fdl::block_attn_bf16_merge_kernel<128, 8, 16, 4, 4>(fdl::AttnArgs)", "FETCH_SIZE", 3, 20.0)]
+    rows_w = [("void fdl::block_attn_bf16_kernel<128, 8>(fdl::AttnArgs)", "WRITE_SIZE", 1, 10.0),
+              ("void fdl::block_attn_bf16_merge_kernel<128, 8, 16, 4, 4>(fdl::AttnArgs)", "WRITE_SIZE", 2, 5.0)]
+    cols = ["kernel_name", "counter_name", "dispatch_id", "value"]
+    dbs = []
+    for nm, rows in [("f", rows_f), ("w", rows_w), ("cf", [("copy", "FETCH_SIZE", 1, 512.0)]),
+                     ("cw", [("copy", "WRITE_SIZE", 1, 1024.0)])]:
+        p = str(tmp_path / f"{nm}.db")
+        _sqlite(p, [("counters_collection", cols, rows)])
+        dbs.append(p)
+
+    class A:
+        summarize_pmc = dbs
+        pmc_kernel = "attn"
+        workload = "qwen2.5-7b_long_bs16"
+        pmc_copy_mib = 1
+    bench.summarize_pmc(A)
+    kv = dict(line.split(": ", 1) for line in capsys.readouterr().out.splitlines())
+    # kernel 150 KiB per dispatch + merge 20 KiB, a 1 MiB copy read as 512 KiB -> scale 2
+    assert float(kv["fetch_kib_per_dispatch"]) == 170.0
+    assert float(kv["copy_fetch_scale"]) == 2.0
+    assert int(kv["fetch_bytes_per_dispatch"]) == 170 * 1024 * 2
+    assert int(kv["write_bytes_per_dispatch"]) == 15 * 1024
