@@ -166,49 +166,46 @@ def _oracle_steps(run, steps, kc, vc, length, stage):
 def cpu_baseline(run, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload.
 
-    The sample is the steps of the schedule's first block and of its last
-    block (the cache grown by the appends of every block in between, which
-    the oracle performs untimed), each stage timed on its own (the eq 15
-    decomposition of the Fast-dLLM review, section 7: attention, LM head,
-    select, append); the first block's steps are then re-run on one thread.
-    Steps stop early once `budget_s` seconds have gone by."""
+    The sample is the steps of four blocks of the schedule -- the first, the
+    last and two spread between them -- each from the cache state it has in
+    the schedule (the blocks in between are appended by the oracle, untimed),
+    each stage timed on its own (the eq 15 decomposition of the Fast-dLLM
+    review, section 7: attention, LM head, select, append); the first block's
+    steps are then re-run on one thread.  Steps stop early once `budget_s`
+    seconds have gone by."""
     import numpy as np
     from oracle import fdl_oracle as O
+    from block_diffusion_decoding_attn_amd import synth
     cfg = run.cfg
     cores = host_cores()
     threads = blas_threads()
+    dual = cfg.attn_mode == "dual_cache"
     kc = run.kc_host.float().numpy().copy()
     vc = run.vc_host.float().numpy().copy()
     length = np.full(cfg.batch, cfg.prompt_len)
     blocks = sorted({run.host_inputs[i].block_idx for i in run.step_ids})
-    first = [i for i in run.step_ids if run.host_inputs[i].block_idx == blocks[0]]
-    last = [i for i in run.step_ids if run.host_inputs[i].block_idx == blocks[-1]] if len(blocks) > 1 else []
+    picks = sorted({blocks[0], blocks[len(blocks) // 3], blocks[2 * len(blocks) // 3], blocks[-1]})
     stage = dict(attention=0.0, lm_head=0.0, select=0.0, append=0.0)
     n = commits = above = cands = 0
     t0 = time.perf_counter()
-    for i in first:
-        kc, vc, length, c, a, m = _oracle_steps(run, [i], kc, vc, length, stage)
-        n, commits, above, cands = n + 1, commits + c, above + a, cands + m
+    cur = blocks[0]  # the cache holds every block before `cur`
+    for blk in picks:
         if time.perf_counter() - t0 > budget_s:
             break
-    if last and time.perf_counter() - t0 <= budget_s and cfg.attn_mode != "dual_cache":
-        # the cache of the last block: every earlier block appended (untimed)
-        kc = run.kc_host.float().numpy().copy()
-        vc = run.vc_host.float().numpy().copy()
-        length = np.full(cfg.batch, cfg.prompt_len)
-        for b in range(blocks[-1]):
-            kb, vb = run.kb_host[b] if b in run.kb_host else (None, None)
-            if kb is None:
-                from block_diffusion_decoding_attn_amd import synth
-                kb, vb = synth.block_kv(cfg, b, run.seed)
-            kc, _ = O.kv_append(kc, kb.float().numpy(), length)
-            vc, length = O.kv_append(vc, vb.float().numpy(), length)
-    if last and time.perf_counter() - t0 <= budget_s:
-        for i in last:
+        if dual:
+            length = np.full(cfg.batch, cfg.prompt_len + blk * cfg.block)
+        else:
+            for b in range(cur, blk):  # untimed: the blocks the sample skips
+                kb, vb = run.kb_host[b] if b in run.kb_host else synth.block_kv(cfg, b, run.seed)
+                kc, _ = O.kv_append(kc, kb.float().numpy(), length)
+                vc, length = O.kv_append(vc, vb.float().numpy(), length)
+        for i in [i for i in run.step_ids if run.host_inputs[i].block_idx == blk]:
             kc, vc, length, c, a, m = _oracle_steps(run, [i], kc, vc, length, stage)
             n, commits, above, cands = n + 1, commits + c, above + a, cands + m
             if time.perf_counter() - t0 > budget_s:
                 break
+        cur = blk + 1
+    first = [i for i in run.step_ids if run.host_inputs[i].block_idx == blocks[0]]
     busy = sum(stage.values())
     # one thread, the first block's steps again (bounded by a third of the budget)
     one = None
@@ -229,11 +226,14 @@ def cpu_baseline(run, budget_s: float):
         one = {"value": n1 / sum(st1.values()), "steps": n1}
     except Exception:  # noqa: BLE001
         one = None
-    sample = (f"{n} steps of the {cfg.name} schedule (blocks {blocks[0]} and {blocks[-1]}, the first and last: "
-              f"fp64 numpy oracle of attention, LM head, select, append), {busy:.1f} s; "
+    sample = (f"{n} steps of the {cfg.name} schedule (blocks {', '.join(map(str, picks))} of {len(blocks)}, each "
+              f"from its own cache state: fp64 numpy oracle of attention, LM head, select, append), {busy:.1f} s; "
               f"{commits / busy:.3f} committed tokens/s")
-    return {"value": n / busy, "unit": "steps/s", "cores": cores, "kind": "oracle", "sample": sample,
-            "blas_threads": threads,
+    # cores: the threads the oracle ran on -- its BLAS pool (the LM head's
+    # product; the rest of the oracle is single-threaded numpy), within the
+    # process's CPU affinity, which is reported beside it
+    return {"value": n / busy, "unit": "steps/s", "cores": min(threads, cores), "kind": "oracle", "sample": sample,
+            "affinity_cores": cores, "blas_threads": threads,
             "stage_seconds_per_step": {k: v / max(n, 1) for k, v in stage.items()},
             "committed_tokens_per_s": commits / busy,
             "exceed_tau_fraction": above / max(cands, 1),

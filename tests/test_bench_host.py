@@ -177,3 +177,17 @@ def test_summarize_pmc_scales_by_the_copy(tmp_path, capsys):
     assert float(kv["copy_fetch_scale"]) == 2.0
     assert int(kv["fetch_bytes_per_dispatch"]) == 170 * 1024 * 2
     assert int(kv["write_bytes_per_dispatch"]) == 15 * 1024
+
+
+def test_cpu_baseline_sample_and_cores():
+    """The oracle leg on the CPU: per-stage seconds, the threads it ran on
+    within the affinity mask, blocks taken from their own cache states."""
+    from block_diffusion_decoding_attn_amd.runner import StepRunner
+    cfg = synth.get_config("qwen2.5-1.5b_bs1")
+    run = StepRunner(cfg, device="cpu", keep_host=True)
+    r = bench.cpu_baseline(run, 3.0)
+    assert r["kind"] == "oracle" and r["unit"] == "steps/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= r["affinity_cores"] == bench.host_cores()
+    assert set(r["stage_seconds_per_step"]) == {"attention", "lm_head", "select", "append"}
+    assert "blocks 0," in r["sample"] and "of 8" in r["sample"]
+    assert 0.0 <= r["exceed_tau_fraction"] <= 1.0
