@@ -422,6 +422,17 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds) {
   const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(l) : "memory", "m0");
 }
+// The same from a base address that must be wave-uniform (it is taken from
+// the first active lane into SGPRs) and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, void* lds) {
+  const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
+  const uint64_t p = reinterpret_cast<uint64_t>(sbase);
+  // (readfirstlane returns int: widen through uint32_t, not by sign extension)
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(p))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(p >> 32))));
+  const uint64_t ps = (uint64_t(hi) << 32) | uint64_t(lo);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(ps), "s"(l) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // s_barrier with the compiler kept from moving memory accesses across it
@@ -531,24 +542,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       ld_elem[j] = c * 8;
       ld_lds[j] = (wave_v ? TILEB : 0) + i * 1024;
     }
+    uint32_t ld_voff[IPW];  // byte offset of this lane's chunk from its tile's first row
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) ld_voff[j] = uint32_t(ld_row[j] * DH + ld_elem[j]) * uint32_t(sizeof(T));
     const int ntiles = (k_end - k_begin + TK - 1) / TK;
     u32x4 qf[KSTEPS];  // B operand of S^T = K Q^T: query column l32, d = 16ks + 8h .. + 7
     auto issue = [&](int t) __attribute__((always_inline)) {
       const int key0 = k_begin + t * TK;
       char* sb = smem + (t % NST) * STB;
       const bool fast = key0 + TK <= k_end && (key0 + TK <= lp || key0 >= lp + a.D);
+      if (fast) {
+        // the whole tile in the cache: one wave-uniform base in SGPRs plus the
+        // lane's constant byte offset (no per-lane 64-bit address arithmetic,
+        // which was a fifth of the loop's VALU instructions)
+        const T* const tb = my_cache + size_t(key0) * DH;
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) load_lds16_s(tb, ld_voff[j], sb + ld_lds[j]);
+        return;
+      }
+      // the tile holding the block or the split's end: per-lane rows from the
+      // cache or the block buffer; keys past the split's end read a valid
+      // row, and their scores are masked
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
-        size_t off;     // element offset from my_cache (or my_blk)
-        bool in_blk = false;
-        if (fast) {
-          off = size_t(key0 + ld_row[j]) * DH;
-        } else {
-          // keys past the split's end read a valid row; their scores are masked
-          const int key = min(key0 + ld_row[j], k_end - 1);
-          in_blk = key >= lp && key < lp + a.D;
-          off = size_t(in_blk ? key - lp : key) * DH;
-        }
+        const int key = min(key0 + ld_row[j], k_end - 1);
+        const bool in_blk = key >= lp && key < lp + a.D;
+        const size_t off = size_t(in_blk ? key - lp : key) * DH;  // element offset from my_cache (or my_blk)
         const T* base = pick(in_blk, my_blk, my_cache);
         load_lds16(base + off + ld_elem[j], sb + ld_lds[j]);
       }
