@@ -467,9 +467,11 @@ template <int DH>
 __device__ __forceinline__ int swz_v(int row) { return DH == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
 // Workspace of the bf16 kernel (nsplit > 1): partials of nsplit x KV heads x
-// NW waves, each PSLOT x 64 lanes floats, where a wave's PSLOT = d/2 + 2
-// values per lane are its O^T registers, m and l.
-__host__ __device__ constexpr int attn_pslot(int dh) { return dh / 2 + 2; }
+// NW waves, each PSLOT x 64 lanes 32-bit words, where a wave's PSLOT = d/4 + 2
+// words per lane are its d/2 O^T values divided by the split's row sum l
+// (bf16, two per word: each is a convex combination of V rows, so bf16 keeps
+// its relative precision), then m and l (fp32).
+__host__ __device__ constexpr int attn_pslot(int dh) { return dh / 4 + 2; }
 
 template <int DH, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void block_attn_bf16_kernel(
@@ -715,27 +717,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (wave_live) store_out(o, m, l);
     return;
   }
-  // split partial: this wave's O^T registers, m and l, in the lanes' own
-  // layout (value e of every lane in one 256-byte run); merged by
-  // block_attn_bf16_merge_kernel
+  // split partial: this wave's O^T registers divided by l (bf16 pairs), m and
+  // l, in the lanes' own layout (word w of every lane in one 256-byte run);
+  // merged by block_attn_bf16_merge_kernel.  A split that holds keys has
+  // l >= 1 in every row (its largest score contributes exp2(0) at least).
   if (!wave_live) return;
   constexpr int PS = attn_pslot(DH);
   const int npairs = a.B * a.Hkv;
-  float* pp = a.part_o + ((size_t(split) * npairs + pid) * NW + wave) * PS * 64 + lane;
+  uint32_t* pp = reinterpret_cast<uint32_t*>(a.part_o) + ((size_t(split) * npairs + pid) * NW + wave) * PS * 64 + lane;
   if (k_begin < lk) {
+    const float inv = 1.f / l;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pp[(dt * 16 + e) * 64] = o[dt][e];
+      for (int e = 0; e < 16; e += 2) pp[(dt * 8 + e / 2) * 64] = pack_bf16x2(o[dt][e] * inv, o[dt][e + 1] * inv);
   }
-  pp[(PS - 2) * 64] = m;
-  pp[(PS - 1) * 64] = l;
+  pp[(PS - 2) * 64] = __float_as_uint(m);
+  pp[(PS - 1) * 64] = __float_as_uint(l);
 }
 
 // Merge of the bf16 kernel's split partials: one workgroup per (KV head,
 // 32-row block) of d / (2 NE) waves; wave j of it merges the lanes' values
-// NE j .. NE j + NE - 1 of the attention wave's O^T registers.  Lane = (query
-// column, half) exactly as in the attention kernel, so every load is a
+// NE j .. NE j + NE - 1 of the attention wave's O^T registers (stored as O / l
+// in bf16 pairs), each split weighted by exp2(m_s - max m) l_s.  Lane =
+// (query column, half) exactly as in the attention kernel, so every load is a
 // 256-byte run.  The (m, l) and values of up to U splits are fetched in one
 // round of loads; splits are combined in split order.  Few splits: NE = 16,
 // U = 4, the d / 32 waves of a row block in one workgroup (they share its
@@ -758,16 +763,22 @@ __global__ __launch_bounds__(NWG * 64) void block_attn_bf16_merge_kernel(AttnArg
   float acc[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+  static_assert(NE % 2 == 0, "bf16 pairs");
   for (int s0 = 0; s0 < a.nsplit; s0 += U) {
     float mv[U], lv[U], ov[U][NE];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = s0 + u < a.nsplit;
-      const float* pp = a.part_o + ((size_t(s0 + u) * npairs + pid) * NW + wave) * PS * 64 + lane;
-      mv[u] = ok ? pp[(PS - 2) * 64] : -INFINITY;
-      lv[u] = ok ? pp[(PS - 1) * 64] : 0.f;
+      const uint32_t* pp =
+          reinterpret_cast<const uint32_t*>(a.part_o) + ((size_t(s0 + u) * npairs + pid) * NW + wave) * PS * 64 + lane;
+      mv[u] = ok ? __uint_as_float(pp[(PS - 2) * 64]) : -INFINITY;
+      lv[u] = ok ? __uint_as_float(pp[(PS - 1) * 64]) : 0.f;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) ov[u][e] = ok ? pp[(NE * j + e) * 64] : 0.f;
+      for (int e = 0; e < NE; e += 2) {
+        const uint32_t w = ok ? pp[((NE * j + e) / 2) * 64] : 0u;
+        ov[u][e] = __uint_as_float(w << 16);
+        ov[u][e + 1] = __uint_as_float(w & 0xFFFF0000u);
+      }
     }
     float rmax = mmax;
 #pragma unroll
@@ -783,8 +794,8 @@ __global__ __launch_bounds__(NWG * 64) void block_attn_bf16_merge_kernel(AttnArg
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!(lv[u] > 0.f)) continue;  // an empty split wrote no O
-      const float w = __builtin_amdgcn_exp2f(mv[u] - mmax);
-      lsum += w * lv[u];
+      const float w = __builtin_amdgcn_exp2f(mv[u] - mmax) * lv[u];  // the split's weight; its O is O / l
+      lsum += w;
 #pragma unroll
       for (int e = 0; e < NE; ++e) acc[e] += w * ov[u][e];
     }

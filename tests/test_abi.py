@@ -70,12 +70,12 @@ def test_workspace_sizes(L):
             # split partials (m, l, O) per query row
             assert ws == 0 or ws % (rows * (cfg.head_dim + 2) * 4) == 0
         else:
-            # per split, KV head and 64-lane wave of 32 rows: the wave's O registers,
-            # m and l (d/2 + 2 floats per lane)
+            # per split, KV head and 64-lane wave of 32 rows: the wave's d/2 O values
+            # as bf16 pairs, m and l (d/4 + 2 32-bit words per lane)
             pairs = cfg.batch * cfg.n_kv_heads
             g_rows = cfg.n_q_heads // cfg.n_kv_heads * cfg.sub_block
             nw = 2 if g_rows <= 64 else 4 if g_rows <= 128 else 8
-            per_split = pairs * nw * 64 * (cfg.head_dim // 2 + 2) * 4
+            per_split = pairs * nw * 64 * (cfg.head_dim // 4 + 2) * 4
             assert ws == 0 or (ws % per_split == 0 and ws > 0), (name, ws)
         assert fdl.fdl_conf_select_workspace_size(d, cfg.sub_block) >= cfg.batch * cfg.sub_block * 16
     assert fdl.fdl_block_attn_workspace_size(_dims(batch=0)) == 0
