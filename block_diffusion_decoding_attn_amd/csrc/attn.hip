@@ -22,8 +22,9 @@
 //     sit in the lane that owns that query column, so the online-softmax
 //     rescale needs no shuffles.
 //   * Online softmax in fp32 with exp2 and the log2(e)/sqrt(d) scale folded
-//     into the scores.  Splits write (m, l, unnormalized O) partials that a
-//     second kernel merges in a fixed order (deterministic).
+//     into the scores.  Splits write (m, l, O) partials that a second kernel
+//     merges in a fixed order (deterministic): bf16 data O / l in bf16 pairs
+//     per lane of the attention wave; f32 data unnormalized O per query row.
 #include "common.h"
 
 namespace fdl {
@@ -39,8 +40,8 @@ struct AttnArgs {
   const int32_t* prefix_len;
   void* out;
   float* lse;
-  float* part_o;   // [nsplit][B][Hq][S][d]      (nsplit > 1)
-  float* part_ml;  // [nsplit][B][Hq][S][2]      (m in log2 units, l)
+  float* part_o;   // nsplit > 1: f32 data [nsplit][B][Hq][S][d]; bf16 data the per-lane partials (attn_pslot)
+  float* part_ml;  // f32 data: [nsplit][B][Hq][S][2]      (m in log2 units, l)
   int B, S, Hq, Hkv, G, cap, D;
   int default_lp;
   int dual;
@@ -396,14 +397,12 @@ __global__ __launch_bounds__(NW * 64) void block_attn_kernel(AttnArgs a) {
 // row sum adds the bf16-rounded P that the P.V product uses (v_dot2 of each
 // packed pair with (1, 1)), per lane; the two half-waves combine at the end.
 //
-// Splits: every split writes (m, l, unnormalized O) in the lanes' own
-// register layout (coalesced, no transposition), then counts itself on its
-// KV head's device-scope counter; the split that arrives last merges all
-// splits of the head in split order (deterministic) from L2, writes the
-// output, and resets the counter to zero for the next call.  The splits of a
-// KV head are placed on one XCD (workgroups are dealt round-robin to the 8
-// XCDs; the logical id below groups them), so their partials meet in that
-// XCD's L2.
+// Splits: every split writes O / l (bf16 pairs), m and l in the lanes' own
+// register layout (coalesced, no transposition); block_attn_bf16_merge_kernel
+// combines the splits of each KV head in split order (deterministic).  The
+// splits of a KV head are placed on one XCD (workgroups are dealt
+// round-robin to the 8 XCDs; the logical id below groups them), so they share
+// that XCD's L2 for the block's K/V rows.
 constexpr int NST = 4;  // LDS ring stages (tiles)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
