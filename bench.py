@@ -50,6 +50,15 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "block_diffusion_decoding_attn_amd", "csrc")
 LM_HEAD_SRC = os.path.join(CSRC, "lm_head.hip")
 ATTN_SRC = os.path.join(CSRC, "attn.hip")
+# the sources a kernel's counter summary was taken on (the hash covers them all)
+KERNEL_SOURCES = {"lm_head": [LM_HEAD_SRC], "attn": [ATTN_SRC, os.path.join(CSRC, "kv_tiles.h")]}
+
+
+def source_sha256(kernel):
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES[kernel]:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def pmc_profile(workload, kernel="lm_head"):
@@ -96,7 +105,6 @@ def pmc_traffic(workload, kernel="lm_head", per_launch_units=1):
     workload, or the kernel source changed since.  For the attention the
     summary's figure covers the attention kernel and its split merge."""
     path = pmc_profile(workload, kernel)
-    src = LM_HEAD_SRC if kernel == "lm_head" else ATTN_SRC
     if not os.path.exists(path):
         return None
     kv = {}
@@ -105,8 +113,7 @@ def pmc_traffic(workload, kernel="lm_head", per_launch_units=1):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if kv.get("source_sha256") != sha or kv.get("workload") != workload:
+        if kv.get("source_sha256") != source_sha256(kernel) or kv.get("workload") != workload:
             return None
         fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_scale"])
         write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_scale"])
@@ -386,7 +393,6 @@ def summarize_pmc(args):
     names = ["block_attn_bf16_kernel", "block_attn_bf16_merge_kernel"] if kernel == "attn" else [
         lm_head_kernel_name(__import__("block_diffusion_decoding_attn_amd.synth", fromlist=["x"]).get_config(
             args.workload))]
-    src = ATTN_SRC if kernel == "attn" else LM_HEAD_SRC
 
     def pick(db, counter):
         got = _pmc_per_kernel(db, counter)
@@ -405,9 +411,10 @@ def summarize_pmc(args):
     cal_w = max(_pmc_per_kernel(cal_write_db, "WRITE_SIZE").items(), key=lambda kv: kv[1][1])[1][1]
     mib = args.pmc_copy_mib
     sf, sw = mib * 1024 / cal_f, mib * 1024 / cal_w
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = source_sha256(kernel)
     lines = [f"kernel: {' + '.join(names)}", f"workload: {args.workload}",
-             f"source: {os.path.relpath(src, ROOT)}", f"source_sha256: {sha}",
+             f"source: {' + '.join(os.path.relpath(p, ROOT) for p in KERNEL_SOURCES[kernel])}",
+             f"source_sha256: {sha}",
              f"dispatches_fetch: {nf}", f"dispatches_write: {nw}",
              f"fetch_kib_per_dispatch: {fetch:.1f}", f"write_kib_per_dispatch: {write:.1f}",
              f"copy_fetch_kib_per_dispatch: {cal_f:.1f}", f"copy_write_kib_per_dispatch: {cal_w:.1f}",

@@ -8,16 +8,21 @@
 //
 // gfx950 design: a workgroup of 4 waves owns 128 consecutive query positions
 // of one query head; each wave 32 of them, on 32x32x16 bf16 MFMA in the same
-// S^T = K Q^T / O^T = V^T P^T orientation as the block attention kernel.  The
-// workgroup walks the keys its last position may see in 64-key tiles staged
-// through a double-buffered LDS (V transposed on the way in); each lane masks
-// the keys beyond its own position's block.  The work is MFMA-bound (AI in
-// the hundreds of flop/B), so heads are not grouped: the G query heads of a
-// KV head re-read its K/V from L2.  The register budget is capped at two
-// waves per SIMD (two workgroups per CU, 2 x 68 KB of LDS): one wave's
-// softmax then overlaps the other's MFMA work, which a single wave per SIMD
-// cannot do across its own dependent S -> P -> O chain (measured 1.5-1.75x).
+// S^T = K Q^T / O^T = V^T P^T orientation as the block attention kernel, with
+// its K/V path: 64-key tiles HBM -> LDS by direct-to-LDS loads (a tile wholly
+// below the workgroup's key limit from one wave-uniform base plus per-lane
+// offsets), K rows swizzled for conflict-free fragment reads, V^T operands
+// from transposing LDS reads, two LDS stages (64 KB at d = 128: two
+// workgroups per CU) with the next tile's loads in flight while one is
+// consumed.  The workgroup walks the keys its last position may see; each
+// lane masks the keys beyond its own position's block.  The work is
+// MFMA-bound (AI in the hundreds of flop/B), so heads are not grouped: the G
+// query heads of a KV head re-read its K/V from L2.  Two waves per SIMD (two
+// workgroups per CU): one wave's softmax overlaps the other's MFMA work,
+// which a single wave per SIMD cannot do across its own dependent
+// S -> P -> O chain.
 #include "common.h"
+#include "kv_tiles.h"
 
 namespace fdl {
 
@@ -37,14 +42,17 @@ template <int DH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_bf16_kernel(
     PrefillArgs a) {
   typedef bf16_t T;
-  constexpr int NT = 256, TK = PF_TK;
+  constexpr int NW = 4, TK = PF_TK, NS = 2;
+  constexpr int ROWB = DH * 2;         // bytes per key row
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int KPI = 1024 / ROWB;     // key rows per 1 KB load instruction
+  constexpr int TILEB = TK * ROWB;     // one K (or V) tile
+  constexpr int STB = 2 * TILEB;       // one stage: K tile, then V tile
+  constexpr int IPH = TILEB / 1024;    // load instructions per K (or V) tile
+  constexpr int IPW = 2 * IPH / NW;    // load instructions per wave per stage
+  static_assert(IPH % IPW == 0, "a wave loads only K or only V");
   constexpr int KSTEPS = DH / 16, DT = DH / 32;
-  constexpr int EPC = 8, CPR = DH / EPC;
-  constexpr int KCH = TK * CPR, KCH_T = KCH / NT;
-  constexpr int VU = (TK / 4) * CPR, VU_T = (VU + NT - 1) / NT;
-  constexpr int KST = DH + 8, VST = TK + 4;
-  __shared__ __attribute__((aligned(16))) T Ks[2][TK * KST];
-  __shared__ __attribute__((aligned(16))) T Vt[2][DH * VST];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -64,63 +72,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const T* K = reinterpret_cast<const T*>(a.k) + kvbase;
   const T* V = reinterpret_cast<const T*>(a.v) + kvbase;
 
-  u32x4 qf[KSTEPS];
-  {
-    const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t(b) * a.nq + (qok ? qi : 0)) * a.Hq + hq) * DH;
+  // this lane's share of the wave's load instructions (see the block attention)
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool wave_v = wave_s * IPW >= IPH;
+  const T* const my_src = pick(wave_v, V, K);
+  int ld_row[IPW], ld_lds[IPW];
+  uint32_t ld_voff[IPW];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = qok ? ld16(qp + ks * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < IPW; ++j) {
+    const int i = wave_s * IPW + j - (wave_v ? IPH : 0);
+    const int row = KPI * i + lane / CPR;
+    const int c = (lane % CPR) ^ (wave_v ? swz_v<DH>(row) : swz_k<DH>(row));
+    ld_row[j] = row;
+    ld_lds[j] = (wave_v ? TILEB : 0) + i * 1024;
+    ld_voff[j] = uint32_t(row * DH + c * 8) * uint32_t(sizeof(T));
   }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * TK;
+    char* sb = smem + (t % NS) * STB;
+    if (key0 + TK <= k_end) {
+      const char* const tb = reinterpret_cast<const char*>(my_src + size_t(key0) * DH);
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) load_lds16_s(tb, ld_voff[j], sb + ld_lds[j]);
+      return;
+    }
+    // the last tile: rows past the workgroup's key limit read its last key
+    // (their scores are masked)
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int key = min(key0 + ld_row[j], k_end - 1);
+      load_lds16(reinterpret_cast<const char*>(my_src + size_t(key) * DH) + (ld_voff[j] - ld_row[j] * ROWB),
+                 sb + ld_lds[j]);
+    }
+  };
+  int koff[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + h) ^ swz_k<DH>(l32)) << 4);
+  int voff[DT];
+  {
+    const int grp = lane >> 4, sl = lane & 15, e = sl >> 2, qq = sl & 3;
+    const int row = 4 * (grp >> 1) + e;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + 16 * (grp & 1) + 4 * qq;
+      voff[dt] = row * ROWB + (((d >> 3) ^ swz_v<DH>(row)) << 4) + (d & 7) * 2;
+    }
+  }
+
+  u32x4 qf[KSTEPS];
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY;
+  float lw[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's share of the row sum, four chains
+  const float c = a.scale_log2;
 
-  u32x4 kreg[KCH_T];
-  u32x4 vreg[VU_T][4];
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int c = 0; c < KCH_T; ++c) {
-      const int ch = tid + c * NT, key = key0 + ch / CPR;
-      kreg[c] = key < k_end ? ld16(K + size_t(key) * DH + (ch % CPR) * EPC) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < VU_T; ++u) {
-      const int un = tid + u * NT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + (un % (TK / 4)) * 4 + e;
-        vreg[u][e] = (un < VU && key < k_end) ? ld16(V + size_t(key) * DH + (un / (TK / 4)) * EPC)
-                                               : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < KCH_T; ++c) {
-      const int ch = tid + c * NT;
-      *reinterpret_cast<u32x4*>(&Ks[buf][(ch / CPR) * KST + (ch % CPR) * EPC]) = kreg[c];
-    }
-#pragma unroll
-    for (int u = 0; u < VU_T; ++u) {
-      const int un = tid + u * NT;
-      if (un >= VU) continue;
-      const int k4 = (un % (TK / 4)) * 4, d0 = (un / (TK / 4)) * EPC;
-      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&vreg[u][0]);
-      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&vreg[u][1]);
-      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&vreg[u][2]);
-      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&vreg[u][3]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        u32x2 w;
-        w[0] = uint32_t(e0[x]) | (uint32_t(e1[x]) << 16);
-        w[1] = uint32_t(e2[x]) | (uint32_t(e3[x]) << 16);
-        *reinterpret_cast<u32x2*>(&Vt[buf][(d0 + x) * VST + k4]) = w;
-      }
-    }
-  };
-  auto compute_tile = [&](int buf, int key0) {
+  auto compute_tile = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * TK;
+    const char* Ks = smem + (t % NS) * STB;
+    const char* Vs = Ks + TILEB;
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(&Ks[buf][(kt * 32 + l32) * KST + ks * 16 + 8 * h]);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + kt * 32 * ROWB + koff[ks]);
         s[kt] = mfma32x32x16_bf16(kf, qf[ks], s[kt]);
       }
     // keys beyond this lane's position's block (or the sequence) do not exist for it
@@ -141,65 +153,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int v = 0; v < 16; ++v)
           if (key0 + kt * 32 + (v / 4) * 8 + h * 4 + (v % 4) >= lim) s[kt][v] = -INFINITY;
     }
-    const float c = a.scale_log2;
-    float mx = s[0][0];
+    float mq[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+    for (int qd = 0; qd < 4; ++qd) {
+      const int kt = qd >> 1, v0 = (qd & 1) * 8;
+      mq[qd] = fmaxf(fmaxf(s[kt][v0], s[kt][v0 + 1]), s[kt][v0 + 2]);
+      mq[qd] = fmaxf(fmaxf(mq[qd], s[kt][v0 + 3]), s[kt][v0 + 4]);
+      mq[qd] = fmaxf(fmaxf(mq[qd], s[kt][v0 + 5]), s[kt][v0 + 6]);
+      mq[qd] = fmaxf(mq[qd], s[kt][v0 + 7]);
+    }
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = xor32_max(mx) * c;
     // lazy rescale (see the block attention kernel); a fully masked tile
     // (mx = -inf) leaves the state untouched
     if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
       const float mn = fmaxf(m, mx);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lw[w] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m = mn;
     }
-    float rs = 0.f;
-    const float mneg = -m;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[kt][v], c, mneg));
-        s[kt][v] = p;
-        rs += p;
-      }
-    rs = xor32_sum(rs);
-    l += rs;
+    // a lane that has seen no key yet (only one past the sequence: its
+    // scores are all -inf) gets P = 0
+    const float mneg = m == -INFINITY ? 0.f : -m;
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         u32x4 pf;
-        pf[0] = pack_bf16x2(s[kt][8 * q + 0], s[kt][8 * q + 1]);
-        pf[1] = pack_bf16x2(s[kt][8 * q + 2], s[kt][8 * q + 3]);
-        pf[2] = pack_bf16x2(s[kt][8 * q + 4], s[kt][8 * q + 5]);
-        pf[3] = pack_bf16x2(s[kt][8 * q + 6], s[kt][8 * q + 7]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * q + 2 * w], c, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * q + 2 * w + 1], c, mneg));
+          // (a named value: a bit cast of the vector element pf[w] reads element 0)
+          const uint32_t pw = pack_bf16x2(p0, p1);
+          pf[w] = pw;
+          lw[w] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, lw[w], false);
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const T* row = &Vt[buf][(dt * 32 + l32) * VST + kt * 32 + q * 16 + h * 4];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8);
-          o[dt] = mfma32x32x16_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, o[dt]);
+          const char* vb0 = Vs + (kt * 32 + q * 16) * ROWB + voff[dt];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vb0));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vb0 + 8 * ROWB));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 vf{lo2[0], lo2[1], hi2[0], hi2[1]};
+          o[dt] = mfma32x32x16_bf16(vf, pf, o[dt]);
         }
       }
   };
 
   const int ntiles = (k_end + TK - 1) / TK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile((t + 1) * TK);
-    compute_tile(buf, t * TK);
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+  issue(0);
+  {
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t(b) * a.nq + (qok ? qi : 0)) * a.Hq + hq) * DH;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = qok ? ld16(qp + ks * 16 + 8 * h) : u32x4{0, 0, 0, 0};
   }
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's loads of tile t (the only ones in flight) are done; after the
+    // barrier every wave's are, and every wave is done with tile t - 1, whose
+    // stage the loads of tile t + 1 then refill
+    wait_vm<0>();
+    bare_barrier();
+    if (t + 1 < ntiles) issue(t + 1);
+    compute_tile(t);
+  }
+  const float l = xor32_sum((lw[0] + lw[1]) + (lw[2] + lw[3]));  // both half-waves' shares of the row sum
   if (!qok) return;
   const float inv = 1.f / l;
   T* op = reinterpret_cast<T*>(a.out) + ((size_t(b) * a.nq + qi) * a.Hq + hq) * DH;

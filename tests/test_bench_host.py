@@ -80,7 +80,7 @@ def test_counter_traffic_only_for_its_workload_and_source(name):
     assert kv["workload"] == name
     cfg = synth.get_config(name)
     assert kv["kernel"] == bench.lm_head_kernel_name(cfg)
-    sha = hashlib.sha256(open(bench.LM_HEAD_SRC, "rb").read()).hexdigest()
+    sha = bench.source_sha256("lm_head")
     got = bench.pmc_traffic(name)
     if kv["source_sha256"] != sha:
         assert got is None          # taken on other sources: not reported
@@ -107,7 +107,7 @@ def test_attention_counter_summary_long_context():
     kv = _pmc_fields(path)
     assert kv["workload"] == name
     assert kv["kernel"] == "block_attn_bf16_kernel + block_attn_bf16_merge_kernel"
-    if kv["source_sha256"] != hashlib.sha256(open(bench.ATTN_SRC, "rb").read()).hexdigest():
+    if kv["source_sha256"] != bench.source_sha256("attn"):
         assert bench.pmc_traffic(name, "attn") is None  # taken on other sources: not reported
         pytest.skip("attention counter summary taken on another source")
     cfg = synth.get_config(name)
