@@ -126,28 +126,6 @@ __global__ __launch_bounds__(256) void dec_block_begin_kernel(DecArgs a, int blk
   }
 }
 
-// Step slot: open the gate when some sequence has a masked row in the
-// active sub-block (only live sequences have any).
-__global__ __launch_bounds__(256) void dec_step_begin_kernel(DecArgs a, int blk, int sub) {
-  const size_t off = a.P + size_t(blk) * a.D + size_t(sub) * a.S;
-  int any = 0;
-  for (int b = threadIdx.x; b < a.B; b += 256) {
-    const uint8_t* m = a.masked + size_t(b) * a.cap + off;
-    int live = 0;
-    for (int i = 0; i < a.S; ++i) live |= m[i];
-    if (live) a.seq_steps[b] += 1;
-    any |= live;
-  }
-  any = __syncthreads_or(any);
-  if (threadIdx.x == 0) {
-    a.ctl[C_GATE_STEP] = any;
-    if (any) {
-      a.ctl[C_CUR] = a.ctl[C_STEPS];
-      a.ctl[C_STEPS] += 1;
-    }
-  }
-}
-
 // Block end: a live sequence whose finished block holds EOS stops.
 __global__ __launch_bounds__(256) void dec_block_end_kernel(DecArgs a, int blk) {
   if (gate_closed(a.ctl + C_GATE_BLOCK)) return;
@@ -218,13 +196,56 @@ struct EmbedArgs {
   void* qd;               // Q destination [B][nq][H] for positions qpos0 .. qpos0 + nq - 1, or null
   int qpos0, nq;
   const int32_t* gate;
+  // a step slot's embedding also opens the slot: non-null ctl, then the
+  // active sub-block's rows start at step_off in every sequence's [cap]
+  // masked flags (only live sequences have masked rows)
+  int32_t* ctl;
+  const uint8_t* masked;
+  int32_t* seq_steps;
+  int B, S, step_off;
 };
+
+// Whether some sequence has a masked row in the active sub-block (the step
+// slot's gate); with `count`, also the bookkeeping of an opened slot.  Every
+// workgroup of the step's embedding evaluates the gate itself; workgroup
+// (0, 0) alone writes the gate word the slot's later kernels read and the
+// step counters.
+__device__ __forceinline__ bool step_open(const EmbedArgs& a, bool count) {
+  __shared__ int any_s;
+  if (threadIdx.x < 64) {
+    int any = 0;
+    for (int b = threadIdx.x; b < a.B; b += 64) {
+      const uint8_t* m = a.masked + size_t(b) * a.cap + a.step_off;
+      int live = 0;
+      for (int i = 0; i < a.S; ++i) live |= m[i];
+      if (count && live) a.seq_steps[b] += 1;
+      any |= live;
+    }
+    any = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+    if (threadIdx.x == 0) {
+      any_s = any;
+      if (count) {
+        a.ctl[C_GATE_STEP] = any;
+        if (any) {
+          a.ctl[C_CUR] = a.ctl[C_STEPS];
+          a.ctl[C_STEPS] += 1;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return any_s != 0;
+}
 
 // One workgroup per (position, sequence): the token's embedding row is read
 // once and scattered to its query, key and (reversed) value slices.
 template <typename T>
 __global__ __launch_bounds__(256) void sm_embed_kernel(EmbedArgs a) {
-  if (gate_closed(a.gate)) return;
+  if (a.ctl) {
+    if (!step_open(a, blockIdx.x == 0 && blockIdx.y == 0)) return;
+  } else if (gate_closed(a.gate)) {
+    return;
+  }
   typedef Chunk<T> C;
   constexpr int E = C::E;
   const int i = blockIdx.x, b = blockIdx.y;
@@ -384,14 +405,16 @@ int decode_launch(const fdl_dims& d, const fdl_decode_args& g, void* ws, hipStre
   a.mask_id = g.mask_id; a.eos_id = g.eos_id; a.dual = dual;
 
   EmbedArgs e;
+  e.ctl = nullptr; e.masked = nullptr; e.seq_steps = nullptr; e.B = B; e.S = S; e.step_off = 0;
   e.w = g.w; e.tokens = g.tokens;
   e.cap = cap; e.V = d.vocab; e.H = d.hidden; e.Hkv = d.n_kv_heads; e.dh = d.head_dim; e.mask_id = g.mask_id;
   e.scale = sqrtf(float(d.hidden));
   auto embed = [&](int pos0, int n, void* kd, void* vd, int dcap, int dpos0, void* qd, int qpos0, int nq,
-                   const int32_t* gate) {
+                   const int32_t* gate, int step_off = -1) {
     EmbedArgs ee = e;
     ee.pos0 = pos0; ee.kd = kd; ee.vd = vd; ee.dcap = dcap; ee.dpos0 = dpos0;
     ee.qd = qd; ee.qpos0 = qpos0; ee.nq = nq; ee.gate = gate;
+    if (step_off >= 0) ee.ctl = ctl, ee.masked = g.masked, ee.seq_steps = g.seq_steps, ee.step_off = step_off;
     if (bf) launch_embed<bf16_t>(ee, n, B, st);
     else launch_embed<float>(ee, n, B, st);
   };
@@ -419,8 +442,9 @@ int decode_launch(const fdl_dims& d, const fdl_decode_args& g, void* ws, hipStre
       const int r0 = blk * D + sub * S;
       m.r0 = r0;
       for (int it = 0; it < slots; ++it) {
-        hipLaunchKernelGGL(dec_step_begin_kernel, dim3(1), dim3(256), 0, st, a, blk, sub);
-        embed(bstart, D, kb, vb, D, 0, q, P + r0, S, gate_step);
+        // the step's embedding opens the slot: the gate of the slot's later
+        // kernels and the step counters
+        embed(bstart, D, kb, vb, D, 0, q, P + r0, S, gate_step, P + r0);
         rc = attn_launch(d, blk, q, g.k_cache, g.v_cache, nullptr, kb, vb, o, nullptr, attn_ws,
                          attn_workspace_bytes(d), st, gate_step);
         if (rc != FDL_OK) return rc;
