@@ -337,6 +337,8 @@ def test_lm_head_select_parity(B, R, H, V, dtype, mode):
     (dict(n_q_heads=4, n_kv_heads=4), 0, 196, 196, False),   # v1 refresh: all keys visible
     (dict(head_dim=64, block=16, sub_block=16), 5, 40, 100, True),
     (dict(n_q_heads=28, n_kv_heads=4), 100, 33, 140, True),
+    (dict(), 0, 20, 20, True),                      # fewer keys than one tile
+    (dict(n_q_heads=2, n_kv_heads=1), 0, 64, 64, False),     # exactly one full tile, GQA
 ])
 def test_prefill_attn_parity(kw, q_start, n_q, n_keys, causal):
     dev = _dev()
