@@ -61,7 +61,7 @@ def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
     (dict(dtype="f32", n_q_heads=4, n_kv_heads=2, head_dim=64, sub_block=32, prompt_len=70, gen_len=64), 1, [3, 102]),
     (dict(prompt_len=0, gen_len=32, sub_block=32, n_q_heads=2, n_kv_heads=1), 0, None),      # only the block
     (dict(batch=3, prompt_len=2000, gen_len=64), 1, [2000, 5, 2032]),   # many splits, some empty
-    # more than 128 rows per KV head: the two-group (ping-pong) kernel
+    # more than 128 rows per KV head: the eight-wave kernel (a padding-only wave when 224 rows)
     (dict(n_q_heads=8, n_kv_heads=1, sub_block=32, prompt_len=0, gen_len=32), 0, None),      # 256 rows, one tile
     (dict(n_q_heads=28, n_kv_heads=4, sub_block=32, prompt_len=64, gen_len=64), 0, None),    # two tiles, one split
     (dict(n_q_heads=16, n_kv_heads=2, sub_block=32, prompt_len=200, gen_len=96), 2, [0, 203]),
