@@ -29,7 +29,9 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers owned by the caller (except `dims`, which
  *     is a host pointer read during the call).  The library allocates no
- *     memory and keeps no global mutable state; calls are reentrant.
+ *     memory and keeps no global mutable state; calls are reentrant.  The
+ *     one exception is fdl_lm_head_select_noalloc, whose static scratch
+ *     array (and its per-device address) is shared by every call on a GPU.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *     No call synchronizes with the host or reads device memory back.
  *   - Validation of scalar arguments and pointers happens on the host before
