@@ -73,6 +73,13 @@ def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
     (dict(attn_mode=synth.DUAL_CACHE, n_q_heads=8, n_kv_heads=4, sub_block=32), 1, None),    # DualCache, 64 rows
     (dict(head_dim=64, n_q_heads=2, n_kv_heads=2, sub_block=16), 2, None),                   # d 64, 16 rows
     (dict(n_q_heads=1, n_kv_heads=1, sub_block=8, prompt_len=190, gen_len=64), 0, None),     # 8 rows, 4 tiles
+    # 65-128 rows per KV head: the four-wave kernel (all rows live, a padding wave, d 64,
+    # DualCache, many splits with the one-wave-per-four-values merge)
+    (dict(n_q_heads=4, n_kv_heads=1, sub_block=32), 1, None),                                # 128 rows
+    (dict(n_q_heads=6, n_kv_heads=2, sub_block=32), 2, [0, 163]),                            # 96 rows
+    (dict(n_q_heads=9, n_kv_heads=1, head_dim=64), 1, None),                                 # 72 rows, d 64
+    (dict(attn_mode=synth.DUAL_CACHE, n_q_heads=8, n_kv_heads=2, sub_block=32), 1, None),    # DualCache, 128 rows
+    (dict(n_q_heads=6, n_kv_heads=2, sub_block=32, batch=3, prompt_len=700, gen_len=64), 1, [700, 3, 731]),
 ])
 def test_block_attn_parity(kw, block_idx, prefix):
     cfg = _cfg(**kw)
