@@ -30,7 +30,7 @@ def _cfg(**kw):
     return synth.Config(**base)
 
 
-def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
+def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0, oracle=True):
     dev = _dev()
     d = fdl.make_dims(cfg)
     q = synth.queries(cfg, 7 + block_idx, seed)
@@ -43,6 +43,8 @@ def _attn_case(cfg, block_idx, sub_idx=0, prefix=None, seed=0):
     fdl.fdl_block_attn(d, block_idx, sub_idx, q.to(dev), kc.to(dev), vc.to(dev), pl, kb.to(dev), vb.to(dev),
                        out, lse, ws)
     torch.cuda.synchronize()
+    if not oracle:
+        return out.float().cpu().numpy(), lse.cpu().numpy(), None, None
     lp = prefix if prefix is not None else [cfg.prompt_len + block_idx * cfg.block] * cfg.batch
     ref_o, ref_l = O.block_attention(q, kc, vc, kb, vb, lp, mode=cfg.attn_mode, total_len=cfg.cap)
     return out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l
@@ -107,6 +109,21 @@ def test_block_attn_deterministic():
     a = _attn_case(cfg, 1)[0]
     b = _attn_case(cfg, 1)[0]
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(n_q_heads=8, n_kv_heads=1, sub_block=32),
+                                dict(dtype="f32", n_q_heads=4, n_kv_heads=2, head_dim=64, sub_block=32)])
+def test_block_attn_prefix_out_of_contract(kw):
+    """Per-sequence prefix lengths outside 0 <= Lp <= P + L - D are clamped to
+    that range (the header's contract): the result equals the clamped call's,
+    bit for bit, and the oracle's at the clamped lengths."""
+    cfg = _cfg(**kw)
+    hi = cfg.cap - cfg.block
+    got_o, got_l, _, _ = _attn_case(cfg, 1, prefix=[-7, 10 ** 6], oracle=False)
+    cl_o, cl_l, ref_o, _ = _attn_case(cfg, 1, prefix=[0, hi])
+    np.testing.assert_array_equal(got_o, cl_o)
+    np.testing.assert_array_equal(got_l, cl_l)
+    assert rowwise(got_o, ref_o)["max"] <= TOL[cfg.dtype]
 
 
 @pytest.mark.parametrize("M,H,V,dtype", [
