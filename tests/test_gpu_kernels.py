@@ -213,6 +213,27 @@ def test_conf_select_ties_and_empty():
     assert got["commit"].tolist() == [[0, 1], [0, 0]]
 
 
+@pytest.mark.parametrize("B,R,V", [(3, 8, 5000), (40, 8, 3000), (2, 96, 1000)])   # the three finalize forms
+def test_conf_select_threshold_extremes_and_large_k(B, R, V):
+    """tau = 0 commits every candidate (every confidence is at least 1/V);
+    tau = 1 commits none by threshold, so exactly the most confident candidate
+    of each sequence that has one (the fallback); top-k with k above the
+    candidate count commits every candidate."""
+    rng = np.random.default_rng(B + R + V)
+    masked = (rng.random((B, R)) < 0.6).astype(np.uint8)
+    masked[0, :] = 0                                   # a sequence without candidates
+    masked[1, 0] = 1
+    n_cand = masked.sum(axis=1)
+    for tau, mode, k in [(0.0, O.SELECT_THRESHOLD, 0), (1.0, O.SELECT_THRESHOLD, 0), (0.9, O.SELECT_TOPK, R + 3)]:
+        got, ref, m, t, _ = _select_case(B, R, V, masked, np.full(B, tau), mode, k=k, step=7)
+        np.testing.assert_array_equal(got["token"], ref["token"])
+        st = compare_select(ref, got, m, t, mode, k, 1.0, eps=1e-5)
+        assert st["seq_checked"] >= 1
+        want = np.minimum(n_cand, 1) if tau == 1.0 else n_cand
+        assert got["n_commit"].tolist() == want.tolist(), (tau, mode)
+        assert (got["commit"].astype(bool) <= masked.astype(bool)).all()
+
+
 def test_conf_select_inplace_update():
     B, R, V = 3, 8, 5000
     masked = np.ones((B, R), np.uint8)
