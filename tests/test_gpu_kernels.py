@@ -384,6 +384,9 @@ def test_lm_head_select_parity(B, R, H, V, dtype, mode):
     (dict(n_q_heads=28, n_kv_heads=4), 100, 33, 140, True),
     (dict(), 0, 20, 20, True),                      # fewer keys than one tile
     (dict(n_q_heads=2, n_kv_heads=1), 0, 64, 64, False),     # exactly one full tile, GQA
+    (dict(), 0, 1, 1, True),                        # one query, one key
+    (dict(), 37, 1, 196, False),                    # one query over every key
+    (dict(), 150, 8, 100, True),                    # queries past the last key: each sees all of them
 ])
 def test_prefill_attn_parity(kw, q_start, n_q, n_keys, causal):
     dev = _dev()
@@ -396,5 +399,9 @@ def test_prefill_attn_parity(kw, q_start, n_q, n_keys, causal):
     fdl.fdl_prefill_attn(d, q_start, n_keys, causal, q.to(dev), k.to(dev), v.to(dev), out, lse)
     torch.cuda.synchronize()
     ref_o, ref_l = O.prefill_attention(q, k, v, q_start, n_keys, cfg.block, causal)
-    assert normwise(out.float().cpu().numpy(), ref_o) <= 2e-2
+    got = out.float().cpu().numpy()
+    rw = rowwise(got, ref_o)
+    print(f"prefill {kw} q {q_start}+{n_q} keys {n_keys} causal {causal}: per-row {rw}", flush=True)
+    assert normwise(got, ref_o) <= 2e-2
+    assert rw["max"] <= 2e-2, rw
     assert np.abs(lse.cpu().numpy() - ref_l).max() <= 1e-3 * np.abs(ref_l).max()
