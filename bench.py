@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --decode-loop [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --prefill [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch: block attention over
 the prefix cache + block, LM head, confidence select (with the commit-state
@@ -27,6 +28,11 @@ through fdl_decode (the device-side decode loop with its stand-in model):
 every block, sub-block and step until all positions are committed or EOS
 stops the sequences; K generations are timed after W warmup generations, and
 the line reports steps/s and committed tokens/s of those generations.
+
+With --prefill a timed unit is one fdl_prefill_attn call on the workload's
+multi-block attention: the prompt prefill under the block-causal mask (the v1
+refresh of the whole cache, every key visible, for the DualCache workload);
+the line reports positions/s and the call's MFMA roofline fraction.
 """
 from __future__ import annotations
 
@@ -329,6 +335,76 @@ def bench_decode_loop(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def prefill_shape(cfg):
+    """The multi-block attention a workload runs: the v1 refresh of the whole
+    cache (every key visible) for DualCache, else the prompt prefill under the
+    block-causal mask.  Returns (n_q = n_keys, causal)."""
+    if cfg.attn_mode == "dual_cache":
+        return cfg.cap, False
+    return cfg.prompt_len, True
+
+
+def prefill_pairs(n: int, block: int, causal: bool) -> int:
+    """Visible (query, key) pairs of one head: block-causal position p sees the
+    keys below the end of its block."""
+    if not causal:
+        return n * n
+    return sum(min(n, (p // block + 1) * block) for p in range(n))
+
+
+def bench_prefill(args, cfg):
+    import torch
+    from block_diffusion_decoding_attn_amd import fdl, synth
+
+    if cfg.dtype != "bf16":
+        print("bench.py --prefill: the multi-block attention is bf16 only", file=sys.stderr)
+        sys.exit(2)
+    n, causal = prefill_shape(cfg)
+    d = fdl.make_dims(cfg)
+    dev = torch.device("cuda")
+    q = synth.normal((cfg.batch, n, cfg.n_q_heads, cfg.head_dim), 0, cfg.cfg_id, 40, n, dtype=cfg.torch_dtype).to(dev)
+    k, v = synth.kv_cache(cfg)
+    k, v = k.to(dev), v.to(dev)
+    out = torch.empty_like(q)
+    for _ in range(max(args.warmup, 1)):
+        fdl.fdl_prefill_attn(d, 0, n, causal, q, k, v, out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        fdl.fdl_prefill_attn(d, 0, n, causal, q, k, v, out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = 4.0 * cfg.head_dim * prefill_pairs(n, cfg.block, causal) * cfg.n_q_heads * cfg.batch
+    byts = 2 * (2 * cfg.batch * n * cfg.n_q_heads * cfg.head_dim + 2 * cfg.batch * cfg.n_kv_heads * n * cfg.head_dim)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out_line = {
+        "metric": "multi-block attention positions/s (prompt prefill or v1 refresh)",
+        "value": cfg.batch * n / (ms * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} {'v1 refresh' if not causal else 'prompt prefill'}",
+                   "batch": cfg.batch, "positions": n, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "block": cfg.block, "mask": "block-causal" if causal else "bidirectional",
+                   "timed_unit": "one fdl_prefill_attn call", "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_attn_bf16_kernel (one launch per call)",
+                     "algorithmic_flops": flops, "algorithmic_bytes": byts,
+                     "arithmetic_intensity": flops / byts},
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def calibrate_counters(mib: int, reps: int = 4):
     """A plain device copy that moves exactly `mib` MiB each way, `reps` times:
     under rocprofv3 --pmc FETCH_SIZE (or WRITE_SIZE) it gives the factor
@@ -481,6 +557,8 @@ def main():
                     help="fdl_lm_head + fdl_conf_select (logits materialized) instead of fdl_lm_head_select")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time whole generations through fdl_decode instead of single steps")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time fdl_prefill_attn on the workload's prompt prefill (v1 refresh for DualCache)")
     ap.add_argument("--graph", action="store_true",
                     help="with --decode-loop: capture the generation in a HIP graph and time its replays")
     ap.add_argument("--calibrate-counters", type=int, nargs="?", const=1024, default=None, metavar="MIB",
@@ -523,6 +601,9 @@ def main():
     cfg = synth.get_config(args.workload)
     if args.decode_loop:
         bench_decode_loop(args, cfg)
+        return
+    if args.prefill:
+        bench_prefill(args, cfg)
         return
     t_setup = time.perf_counter()
     run = StepRunner(cfg, select=args.select, k=args.k, boost=args.boost, keep_host=not args.no_cpu_baseline,

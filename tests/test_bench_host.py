@@ -194,3 +194,17 @@ def test_cpu_baseline_sample_and_cores():
     assert set(r["stage_seconds_per_step"]) == {"attention", "lm_head", "select", "append"}
     assert "blocks 0," in r["sample"] and "of 8" in r["sample"]
     assert 0.0 <= r["exceed_tau_fraction"] <= 1.0
+
+
+def test_prefill_shape_and_pairs():
+    """The multi-block bench line: prompt prefill under the block-causal mask,
+    the whole cache bidirectionally for DualCache; visible pairs counted by
+    brute force over the mask on small sizes."""
+    from block_diffusion_decoding_attn_amd import synth
+    assert bench.prefill_shape(synth.get_config("qwen2.5-7b_bs4")) == (1024, True)
+    llada = synth.get_config("llada-8b_dualcache")
+    assert bench.prefill_shape(llada) == (llada.cap, False)
+    for n, blk in [(1, 32), (31, 32), (64, 32), (100, 16), (257, 32)]:
+        brute = sum(1 for p in range(n) for j in range(n) if j // blk <= p // blk)
+        assert bench.prefill_pairs(n, blk, True) == brute
+        assert bench.prefill_pairs(n, blk, False) == n * n
